@@ -1,0 +1,23 @@
+"""Float64 CPU oracle for online-softmax attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the HIP library or its binding.
+"""
+from .attention import (  # noqa: F401
+    NEG_INF,
+    allowed_keys,
+    attention_bwd_ref,
+    attention_monoid,
+    attention_ref,
+    block_state,
+    decode_combine,
+    decode_partials,
+    decode_ref,
+    finalize,
+    identity_state,
+    mask_matrix,
+    merge,
+    online_softmax_recurrence,
+    scores,
+    split_bounds,
+)

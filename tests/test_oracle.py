@@ -1,0 +1,10 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+import oracle.attention as A
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(A)
