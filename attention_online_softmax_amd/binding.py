@@ -1,0 +1,182 @@
+"""ctypes binding over libattn.so: argument marshalling only.
+
+Every function here checks that tensors are contiguous device tensors of one
+dtype, allocates outputs and workspaces with torch when the caller does not
+pass them, and calls the C entry point of the same name on torch's current
+stream.  All arithmetic happens in the HIP kernels; there is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_ALIAS", 6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_HIP",
+    8: "ATTN_ERR_VALUE",
+}
+EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
+           "attn_decode_workspace_bytes", "attn_decode", "attn_bwd_workspace_bytes", "attn_bwd")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({attn_status_str(status)})")
+
+
+def lib():
+    """Load libattn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m attention_online_softmax_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_abi_version.restype = i
+    L.attn_abi_version.argtypes = []
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_status_str.argtypes = [i]
+    L.attn_supports.restype = i
+    L.attn_supports.argtypes = [i, i, i]
+    L.attn_fwd.restype = i
+    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_decode.restype = i
+    L.attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_bwd.restype = i
+    L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                           i, i, i, i, i, i, i, f, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def attn_abi_version():
+    return lib().attn_abi_version()
+
+
+def attn_status_str(status):
+    return lib().attn_status_str(int(status)).decode()
+
+
+def attn_supports(dtype, entry, d):
+    return bool(lib().attn_supports(int(dtype), int(entry), int(d)))
+
+
+def attn_decode_workspace_bytes(B, Hq, d, n_splits):
+    return int(lib().attn_decode_workspace_bytes(B, Hq, d, n_splits))
+
+
+def attn_bwd_workspace_bytes(B, Hq, Sq, d):
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Sq, d))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(ts, names):
+    dev = ts[0].device
+    for t, nm in zip(ts, names):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{nm} must be a tensor")
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError(f"{nm} must be on the same GPU as {names[0]}")
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, want_lse=True):
+    """Forward prefill.  q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d]; returns (o, lse)."""
+    _check([q, k, v], ["q", "k", "v"])
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    dt = _dtype_code(q)
+    st = lib().attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                        B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), float(scale),
+                        _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_fwd")
+    return o, lse
+
+
+def attn_decode(q, k_cache, v_cache, scale=None, n_splits=16, o=None, lse=None,
+                workspace=None, stream=None):
+    """Split-KV decode.  q [B,Hq,1,d], caches [B,Hkv,Skv,d]; returns (o, lse)."""
+    _check([q, k_cache, v_cache], ["q", "k_cache", "v_cache"])
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per head: q must be [B, Hq, 1, d]")
+    Hkv, Skv = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, 1), device=q.device, dtype=torch.float32)
+    need = attn_decode_workspace_bytes(B, Hq, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    st = lib().attn_decode(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                           _ptr(lse), B, Hq, Hkv, Skv, d, float(scale), int(n_splits),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_decode")
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Backward.  Returns (dq, dk, dv)."""
+    _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, Sq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    st = lib().attn_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                        _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
+                        int(bool(causal)), float(scale), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

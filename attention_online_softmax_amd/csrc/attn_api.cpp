@@ -1,0 +1,183 @@
+// C ABI of libattn.so: argument validation and dispatch.  Every check runs
+// on the host before anything is enqueued, so a rejected call launches
+// nothing ("Compilers and Kernels", section "A kernel implements a bounded
+// contract": a specialised kernel must guard shape, stride, dtype, layout
+// and aliasing facts or keep a general path; this library guards them and
+// reports an error instead of guessing).
+#include "../../include/attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxSplits = 256;
+constexpr int kDecodeMaxChunk = 1024;
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
+
+bool fwd_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
+bool decode_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
+bool bwd_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
+
+// Per-head element counts must stay within 32-bit index arithmetic.
+bool sizes_ok(int64_t S, int d) { return S * (int64_t)d < (int64_t(1) << 31); }
+
+// Outputs must not overlap inputs or each other.
+attn_status check_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (int j = 0; j < n_in; ++j)
+      if (ins[j].lo != ins[j].hi && overlap(outs[i], ins[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (outs[j].lo != outs[j].hi && overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+  }
+  return ATTN_OK;
+}
+
+attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char* attn_status_str(int s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (non-positive size, Hq % Hkv != 0, causal with Sq > Skv, or too large)";
+    case ATTN_ERR_UNSUPPORTED: return "head dim or dtype not compiled for this entry point";
+    case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_VALUE: return "invalid scalar argument (scale not finite or n_splits out of range)";
+  }
+  return "unknown status";
+}
+
+int attn_supports(int dtype, int entry, int d) {
+  switch (entry) {
+    case 0: return fwd_d_ok(dtype, d);
+    case 1: return decode_d_ok(dtype, d);
+    case 2: return bwd_d_ok(dtype, d);
+  }
+  return 0;
+}
+
+attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+                     void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  if (!fwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return ATTN_ERR_ALIGN;
+  const int es = esize(dtype);
+  const Span ins[3] = {span(q, (int64_t)B * Hq * Sq * d * es), span(k, (int64_t)B * Hkv * Skv * d * es),
+                       span(v, (int64_t)B * Hkv * Skv * d * es)};
+  const Span outs[2] = {span(o, (int64_t)B * Hq * Sq * d * es),
+                        lse ? span(lse, (int64_t)B * Hq * Sq * 4) : Span{0, 0}};
+  attn_status st = check_alias(outs, 2, ins, 3);
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{dtype, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0, scale,
+                  (hipStream_t)stream};
+  return hip_status(attn::launch_fwd(a));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int n_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || n_splits <= 0) return 0;
+  return round256((size_t)n_splits * B * Hq * (size_t)(d + 2) * sizeof(float));
+}
+
+attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
+                        float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                        int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  if (!decode_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_VALUE;
+  if ((Skv + n_splits - 1) / n_splits > kDecodeMaxChunk) return ATTN_ERR_VALUE;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, d, n_splits)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  const int es = esize(dtype);
+  const Span ins[3] = {span(q, (int64_t)B * Hq * d * es),
+                       span(k_cache, (int64_t)B * Hkv * Skv * d * es),
+                       span(v_cache, (int64_t)B * Hkv * Skv * d * es)};
+  const Span outs[3] = {span(o, (int64_t)B * Hq * d * es),
+                        lse ? span(lse, (int64_t)B * Hq * 4) : Span{0, 0},
+                        span(workspace, (int64_t)attn_decode_workspace_bytes(B, Hq, d, n_splits))};
+  attn_status st = check_alias(outs, 3, ins, 3);
+  if (st != ATTN_OK) return st;
+  attn::DecodeArgs a{dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, n_splits, scale,
+                     (float*)workspace, (hipStream_t)stream};
+  return hip_status(attn::launch_decode(a));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0) return 0;
+  return round256((size_t)B * Hq * Sq * sizeof(float));
+}
+
+attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+                     const void* d_o, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  if (!bwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Sq, d)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  const int es = esize(dtype);
+  const int64_t nq = (int64_t)B * Hq * Sq * d * es, nkv = (int64_t)B * Hkv * Skv * d * es;
+  const Span ins[6] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
+                       span(lse, (int64_t)B * Hq * Sq * 4)};
+  const Span outs[4] = {span(dq, nq), span(dk, nkv), span(dv, nkv),
+                        span(workspace, (int64_t)attn_bwd_workspace_bytes(B, Hq, Sq, d))};
+  attn_status st = check_alias(outs, 4, ins, 6);
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
+                  causal ? 1 : 0, scale, (float*)workspace, (hipStream_t)stream};
+  return hip_status(attn::launch_bwd(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launch descriptors passed from the C ABI layer to the kernel
+// launchers.  Arguments are validated before any of these is filled in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct FwdArgs {
+  int dtype;  // 0 = f32, 1 = bf16
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Skv, d, causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  int dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Skv, d, n_splits;
+  float scale;
+  float* ws;  // [n_splits, B, Hq] m, then l, then [n_splits, B, Hq, d] acc
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  int dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Sq, Skv, d, causal;
+  float scale;
+  float* ws;  // [B, Hq, Sq] D = rowsum(dO * O)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+
+}  // namespace attn

@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of the online-softmax attention library (libattn.so).
+ *
+ * Computes scaled dot-product attention O = softmax(scale * Q K^T + C) V in
+ * one pass over the keys, the way "Compilers and Kernels" (section
+ * "FlashAttention changes the algorithm around IO") defines it: first display
+ * equation for the function, second display equation for the blockwise
+ * recurrence of running maximum m, normaliser l and accumulator o, and
+ * O_i = o_T / l_T at the end.  Partial states over disjoint key ranges are
+ * combined by the online-softmax monoid ("Tang, a compiler that derives GPU
+ * kernels and bounds how fast they can run", Abstract): both sides are
+ * rescaled to the larger maximum and added.  No score or probability matrix
+ * is ever written to device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  q, k, v, o, lse and the gradient buffers are DEVICE pointers
+ *   (memory from hipMalloc or a framework allocator on the current device).
+ *   The caller owns every buffer, including workspaces; the library never
+ *   allocates or frees device memory, keeps no state between calls and does
+ *   not synchronise.
+ * Layout.  Dense, contiguous [B, H, S, d] (d innermost) for Q, K, V, O, dO,
+ *   dQ, dK, dV; [B, Hq, Sq] float32 for LSE.  K and V share Hkv heads; query
+ *   head h reads key/value head h / (Hq / Hkv) (grouped-query attention).
+ * Dtypes.  ATTN_F32: float32 storage and float32 arithmetic throughout.
+ *   ATTN_BF16: bfloat16 storage, bf16 matrix-core products with float32
+ *   accumulation and float32 softmax statistics.  O, dQ, dK, dV take the
+ *   input dtype (bf16 results rounded to nearest even); LSE is float32.
+ * Mask.  causal != 0 allows key j for query i iff j <= i + (Skv - Sq)
+ *   (bottom-right alignment; the usual lower triangle when Sq == Skv).  The
+ *   definition requires every query row to keep at least one allowed key,
+ *   so causal with Sq > Skv is rejected.
+ * LSE.  lse[i] = m_i + ln(l_i): natural-log log-sum-exp of the scaled,
+ *   masked scores of row i ("Don't Write Kernels, Derive Them", "What
+ *   happened": logsumexp).
+ * Scale.  Multiplies the exact dot product; must be finite.
+ * Alignment.  Every pointer must be 16-byte aligned (128-bit accesses).
+ * Aliasing.  No output may overlap an input or another output.
+ * Stream.  `stream` is a hipStream_t (NULL = default stream).  Work is
+ *   enqueued on it; results are valid once the stream passes the call.
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ *   on any error nothing is launched and a nonzero attn_status is returned.
+ *   ATTN_ERR_HIP reports a failed launch (hipGetLastError) and then the
+ *   state of the outputs is undefined.
+ * Numerics.  Forward and decode are deterministic for fixed shapes and
+ *   n_splits.  The backward writes each gradient element once (no atomics)
+ *   and is deterministic too.  Inputs must be finite.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, causal Sq>Skv,
+                               sizes beyond the 32-bit per-head index range     */
+  ATTN_ERR_UNSUPPORTED = 3, /* head dim or dtype outside the compiled set       */
+  ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
+  ATTN_ERR_ALIAS = 5,       /* an output overlaps an input or another output    */
+  ATTN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+  ATTN_ERR_HIP = 7,         /* a HIP launch failed                              */
+  ATTN_ERR_VALUE = 8        /* a scalar argument is invalid (scale not finite,
+                               n_splits out of range)                           */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_status_str(int status);
+
+/* Head dims compiled for (dtype, entry point): returns 1 if supported.
+ * entry: 0 = attn_fwd, 1 = attn_decode, 2 = attn_bwd. */
+int attn_supports(int dtype, int entry, int d);
+
+/*
+ * Forward prefill.  For every (b, h, i): O[b,h,i,:] and lse[b,h,i] of the
+ * attention of query row i over the allowed keys of K/V head h / (Hq/Hkv).
+ *   q   [B, Hq,  Sq,  d]   input
+ *   k   [B, Hkv, Skv, d]   input
+ *   v   [B, Hkv, Skv, d]   input
+ *   o   [B, Hq,  Sq,  d]   output, dtype of the inputs
+ *   lse [B, Hq,  Sq]       output, float32 (may be NULL if not wanted)
+ * Computed as the blockwise recurrence of the second display equation of
+ * "Compilers and Kernels", FlashAttention section, one query tile per
+ * workgroup.  Supported d: f32 {64, 128, 256}; bf16 {64, 128, 256}.
+ */
+attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v,
+                     void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                     int causal, float scale, void* stream);
+
+/* Workspace for attn_decode: n_splits * B * Hq * (d + 2) float32 values,
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int n_splits);
+
+/*
+ * Split-KV decode: one new query token per (batch, query head) against a
+ * contiguous KV cache whose Skv keys are all visible (the cache already
+ * holds the current token; no mask).
+ *   q        [B, Hq, 1, d]     input
+ *   k_cache  [B, Hkv, Skv, d]  input
+ *   v_cache  [B, Hkv, Skv, d]  input
+ *   o        [B, Hq, 1, d]     output, dtype of the inputs
+ *   lse      [B, Hq, 1]        output, float32 (may be NULL)
+ *   workspace >= attn_decode_workspace_bytes(B, Hq, d, n_splits) bytes of
+ *             device memory, 16-byte aligned; contents on entry are ignored
+ *             and on exit unspecified.
+ * The keys are cut into n_splits contiguous chunks of ceil(Skv / n_splits)
+ * keys (trailing chunks may be short or empty).  A first kernel computes each
+ * chunk's unnormalised state (m, l, acc) for all Hq / Hkv query heads of a
+ * key/value head in one pass over that chunk's keys and values; a second
+ * kernel folds the n_splits states of each query with the monoid merge and
+ * writes O = acc / l and lse = m + ln l.  1 <= n_splits <= 256 and
+ * ceil(Skv / n_splits) <= 1024 (one chunk's scores live in LDS), else
+ * ATTN_ERR_VALUE.
+ * Supported d: {64, 128, 256} for both dtypes.
+ */
+attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse,
+                        int B, int Hq, int Hkv, int Skv, int d, float scale, int n_splits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for attn_bwd: B * Hq * Sq float32 values (D_i = dO_i . O_i),
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
+
+/*
+ * Backward.  Gradients of O = softmax(scale Q K^T + C) V given dO, with the
+ * probabilities recomputed from the saved lse instead of being stored
+ * ("Compilers and Kernels", FlashAttention section, closing paragraph; the
+ * "Tang" Abstract: gradients of comprehensions are comprehensions):
+ *   P = exp(scale Q K^T + C - lse), dV = P^T dO, dP = dO V^T,
+ *   D_i = dO_i . O_i, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q;
+ * for grouped heads dK, dV of a key/value head sum over its query heads.
+ *   q, k, v, o, d_o   inputs (o and lse as returned by attn_fwd)
+ *   lse [B, Hq, Sq]   float32 input
+ *   dq  [B, Hq, Sq, d], dk, dv [B, Hkv, Skv, d]   outputs, input dtype
+ *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned.
+ * Supported: bf16 with d in {64, 128}.
+ */
+attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
+                     const void* o, const void* d_o, const float* lse,
+                     void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                     int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

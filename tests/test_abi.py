@@ -1,0 +1,168 @@
+"""C ABI contract checks that need no GPU.
+
+The library must load, export every function include/attn.h declares, and
+reject invalid arguments on the host before any HIP call (so these calls use
+fake, never-dereferenced device addresses).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_online_softmax_amd as aos
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(aos.LIB_PATH),
+                                reason="libattn.so not built (run __graft_entry__.build())")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS, HIP, VALUE = range(9)
+F32, BF16 = 0, 1
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = aos.lib()
+    names = declared_functions()
+    assert set(names) == set(aos.EXPORTS), names
+    for nm in names:
+        assert hasattr(L, nm), f"missing export {nm}"
+
+
+def test_version_and_strings():
+    assert aos.attn_abi_version() == 1
+    for s in range(9):
+        assert aos.attn_status_str(s) and aos.attn_status_str(s) != "unknown status"
+    assert aos.attn_status_str(99) == "unknown status"
+
+
+def test_supports():
+    for d in (64, 128, 256):
+        assert aos.attn_supports(F32, 0, d) and aos.attn_supports(BF16, 0, d)
+        assert aos.attn_supports(F32, 1, d) and aos.attn_supports(BF16, 1, d)
+    assert aos.attn_supports(BF16, 2, 64) and aos.attn_supports(BF16, 2, 128)
+    assert not aos.attn_supports(BF16, 2, 256)
+    assert not aos.attn_supports(BF16, 0, 96)
+    assert not aos.attn_supports(7, 0, 64)
+
+
+def test_workspace_sizes():
+    assert aos.attn_decode_workspace_bytes(8, 32, 128, 16) == 16 * 8 * 32 * 130 * 4
+    assert aos.attn_decode_workspace_bytes(1, 1, 64, 1) == 512      # 66*4 rounded to 256
+    assert aos.attn_decode_workspace_bytes(0, 1, 64, 1) == 0
+    assert aos.attn_bwd_workspace_bytes(4, 16, 2048, 128) == 4 * 16 * 2048 * 4
+    assert aos.attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
+    assert aos.attn_bwd_workspace_bytes(1, -1, 1, 64) == 0
+
+
+class Fake:
+    """Disjoint, 16-byte aligned fake device addresses (never dereferenced)."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes=64 * MB):
+        p = self.next
+        self.next += nbytes + 4096
+        return p
+
+
+def fwd(dt=BF16, q=1, k=1, v=1, o=1, lse=1, B=1, Hq=2, Hkv=1, Sq=8, Skv=8, d=64, causal=0,
+        scale=0.125):
+    return aos.lib().attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, scale, None)
+
+
+def test_fwd_validation():
+    f = Fake()
+    p = {n: f() for n in ("q", "k", "v", "o", "lse")}
+    assert fwd(q=None, k=p["k"], v=p["v"], o=p["o"], lse=p["lse"]) == NULL
+    base = dict(q=p["q"], k=p["k"], v=p["v"], o=p["o"], lse=p["lse"])
+    assert fwd(**base, B=0) == SHAPE
+    assert fwd(**base, Sq=0) == SHAPE
+    assert fwd(**base, Hq=3, Hkv=2) == SHAPE
+    assert fwd(**base, Sq=9, Skv=8, causal=1) == SHAPE
+    assert fwd(**base, d=96) == UNSUP
+    assert fwd(**base, dt=5) == UNSUP
+    assert fwd(**base, scale=float("nan")) == VALUE
+    assert fwd(**base, scale=float("inf")) == VALUE
+    assert fwd(**dict(base, o=p["o"] + 8)) == ALIGN
+    assert fwd(**dict(base, lse=p["lse"] + 4)) == ALIGN
+    assert fwd(**dict(base, o=p["q"])) == ALIAS                        # output over input
+    assert fwd(**dict(base, o=p["q"] + 16 * 64 * 2 - 16)) == ALIAS     # partial overlap
+    assert fwd(**dict(base, lse=p["o"] + 16)) == ALIAS                 # outputs overlap
+    assert fwd(**base, Sq=1 << 30, Skv=1 << 30) == SHAPE               # beyond 32-bit per head
+
+
+def test_decode_validation():
+    f = Fake()
+    q, k, v, o, lse, ws = (f() for _ in range(6))
+    need = aos.attn_decode_workspace_bytes(2, 8, 128, 16)
+    L = aos.lib()
+
+    def call(**kw):
+        a = dict(dt=BF16, q=q, k=k, v=v, o=o, lse=lse, B=2, Hq=8, Hkv=2, Skv=4096, d=128,
+                 scale=0.1, n=16, ws=ws, wsb=need)
+        a.update(kw)
+        return L.attn_decode(a["dt"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                             a["Hkv"], a["Skv"], a["d"], a["scale"], a["n"], a["ws"], a["wsb"],
+                             None)
+
+    assert call(k=None) == NULL
+    assert call(Hq=6, Hkv=4) == SHAPE
+    assert call(Skv=0) == SHAPE
+    assert call(d=80) == UNSUP
+    assert call(n=0) == VALUE
+    assert call(n=257) == VALUE
+    assert call(Skv=1 << 20, n=16) == VALUE          # chunk above the per-workgroup limit
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=ws + 8) == ALIGN
+    assert call(ws=k) == ALIAS
+    assert call(o=q) == ALIAS
+    assert call(scale=float("-inf")) == VALUE
+
+
+def test_bwd_validation():
+    f = Fake()
+    names = ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws")
+    p = {n: f() for n in names}
+    need = aos.attn_bwd_workspace_bytes(1, 4, 64, 128)
+    L = aos.lib()
+
+    def call(**kw):
+        a = dict(p)
+        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, scale=0.1,
+                      wsb=need))
+        a.update(kw)
+        return L.attn_bwd(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                          a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["d"],
+                          a["causal"], a["scale"], a["ws"], a["wsb"], None)
+
+    for n in names[:-1]:
+        assert call(**{n: None}) == NULL, n
+    assert call(Sq=65) == SHAPE
+    assert call(Hq=5) == SHAPE
+    assert call(d=256) == UNSUP
+    assert call(dt=F32) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=16) == WS
+    assert call(dk=p["dv"]) == ALIAS
+    assert call(dq=p["do"]) == ALIAS
+    assert call(ws=p["lse"]) == ALIAS
+    assert call(dv=p["dv"] + 2) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import attention_online_softmax_amd.binding as bnd
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        bnd.lib()
