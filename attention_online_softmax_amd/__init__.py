@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     attn_decode,
     attn_decode_workspace_bytes,
     attn_fwd,
+    attn_set_timing_events,
     attn_status_str,
     attn_supports,
     lib,

@@ -23,7 +23,8 @@ STATUS_NAMES = {
     8: "ATTN_ERR_VALUE",
 }
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_bwd_workspace_bytes", "attn_bwd")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_bwd_workspace_bytes", "attn_bwd",
+           "attn_set_timing_events")
 
 _lib = None
 
@@ -61,6 +62,8 @@ def lib():
     L.attn_bwd.restype = i
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                            i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.attn_set_timing_events.restype = i
+    L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
     return L
 
@@ -75,6 +78,19 @@ def attn_status_str(status):
 
 def attn_supports(dtype, entry, d):
     return bool(lib().attn_supports(int(dtype), int(entry), int(d)))
+
+
+def attn_set_timing_events(events):
+    """events: sequence of raw hipEvent_t handles (ints), or None to stop.
+    Slot 2i is recorded before and 2i+1 after the i-th kernel of each call."""
+    if not events:
+        st = lib().attn_set_timing_events(None, 0)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        attn_set_timing_events._keep = arr  # the library keeps the pointer
+        st = lib().attn_set_timing_events(arr, len(events))
+    if st:
+        raise AttnError(st, "attn_set_timing_events")
 
 
 def attn_decode_workspace_bytes(B, Hq, d, n_splits):

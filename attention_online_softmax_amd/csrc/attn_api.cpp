@@ -57,7 +57,17 @@ attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+thread_local void* const* g_events = nullptr;
+thread_local int g_n_events = 0;
+
 }  // namespace
+
+namespace attn {
+void timing_mark(hipStream_t stream, int slot) {
+  if (g_events && slot < g_n_events && g_events[slot])
+    (void)hipEventRecord((hipEvent_t)g_events[slot], stream);
+}
+}  // namespace attn
 
 extern "C" {
 
@@ -76,6 +86,13 @@ const char* attn_status_str(int s) {
     case ATTN_ERR_VALUE: return "invalid scalar argument (scale not finite or n_splits out of range)";
   }
   return "unknown status";
+}
+
+attn_status attn_set_timing_events(void* const* events, int n) {
+  if (n < 0) return ATTN_ERR_VALUE;
+  g_events = (events && n > 0) ? events : nullptr;
+  g_n_events = g_events ? n : 0;
+  return ATTN_OK;
 }
 
 int attn_supports(int dtype, int entry, int d) {

@@ -312,24 +312,30 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   constexpr int RPB = 256 / (D / 8);
+  timing_mark(a.stream, 0);
   hipLaunchKernelGGL((bwd_dot_do_o_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
                      a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.ws, rows);
+  timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const int n_ktiles = (a.Skv + 127) / 128;
+  timing_mark(a.stream, 2);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * a.B * a.Hkv), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, a.lse, (const float*)a.ws, (uint16_t*)a.dk,
                      (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, n_ktiles);
+  timing_mark(a.stream, 3);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
+  timing_mark(a.stream, 4);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, a.lse, (const float*)a.ws, (uint16_t*)a.dq, BH,
                      a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, n_qtiles);
+  timing_mark(a.stream, 5);
   return hipGetLastError();
 }
 

@@ -245,13 +245,17 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int n_hchunks = (G + GC - 1) / GC;
   const int chunk = (a.Skv + a.n_splits - 1) / a.n_splits;
   dim3 grid(a.n_splits, a.Hkv * n_hchunks, a.B);
+  timing_mark(a.stream, 0);
   hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), grid, dim3(kDecodeThreads), 0, a.stream,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, a.ws, a.B, a.Hq, a.Hkv, a.Skv,
                      chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
+  timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  timing_mark(a.stream, 2);
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, a.stream,
                      (const float*)a.ws, (T*)a.o, a.lse, a.B * a.Hq, a.n_splits);
+  timing_mark(a.stream, 3);
   return hipGetLastError();
 }
 

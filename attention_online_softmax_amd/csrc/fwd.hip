@@ -290,9 +290,11 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   constexpr int ROWS = 256 / (D / 32);
   const int n_qtiles = (a.Sq + ROWS - 1) / ROWS;
   const int BH = a.B * a.Hq;
+  timing_mark(a.stream, 0);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e, n_qtiles);
+  timing_mark(a.stream, 1);
   return hipGetLastError();
 }
 
@@ -300,10 +302,12 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
+  timing_mark(a.stream, 0);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e,
                      n_qtiles);
+  timing_mark(a.stream, 1);
   return hipGetLastError();
 }
 

@@ -49,6 +49,10 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Records the caller's timing event for `slot` (2i before / 2i+1 after the
+// i-th kernel of the current entry point) if timing events are set.
+void timing_mark(hipStream_t stream, int slot);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);

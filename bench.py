@@ -1,0 +1,431 @@
+"""Benchmark of the online-softmax attention hot path on one MI355X.
+
+One step = attn_fwd followed by attn_bwd on the training workload
+(bf16, causal, B=4, H=16, S=2048, d=128): every row of the path except
+split-KV decode, which is timed in the same run on its own workload
+(bf16, B=8, Hq=32, Hkv=8, Skv=4096, d=128, 16 splits), as is the 44k-token
+head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
+resident in device memory; three input sets rotate so that no step reuses
+the previous step's data from the 256 MiB last-level cache.
+
+Prints one JSON line.  `value` = algorithmic TFLOP/s of the step (forward
+4*d, backward 10*d FLOP per allowed (query, key) pair per head).  The
+`roofline` object is for the kernel that takes the most time per step,
+timed with HIP events recorded around that kernel inside the timed region.
+`cpu_baseline` times the float64 oracle on a bounded sample on host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extras] [--only fwd_bwd|decode|prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak; decode HBM GB/s + % peak"
+
+# Kernel names as they appear in a rocprofv3 kernel trace, per ABI call
+# (the i-th kernel of each call, matching the timing-event slots).
+KERNELS = {
+    "fwd": ["fwd_bf16_kernel"],
+    "bwd": ["bwd_dot_do_o_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+    "decode": ["decode_split_kernel", "decode_combine_kernel"],
+}
+SOURCES = {"fwd_bf16_kernel": "fwd.hip", "bwd_dot_do_o_kernel": "bwd.hip",
+           "bwd_dkdv_kernel": "bwd.hip", "bwd_dq_kernel": "bwd.hip",
+           "decode_split_kernel": "decode.hip", "decode_combine_kernel": "decode.hip"}
+
+
+class HipEvents:
+    """Timing events: torch's HIP events (the process's one HIP runtime),
+    handed to the library by their raw hipEvent_t handles."""
+
+    def __init__(self):
+        self.made = []
+
+    def create(self, n):
+        import torch
+        out = []
+        for _ in range(n):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()  # creates the underlying hipEvent_t
+            out.append(e)
+        torch.cuda.synchronize()
+        for e in out:
+            if not e.cuda_event:
+                raise RuntimeError("could not create a HIP event")
+        self.made += out
+        return out
+
+    @staticmethod
+    def handles(events):
+        return [e.cuda_event for e in events]
+
+    @staticmethod
+    def record(ev, stream):
+        ev.record(stream)
+
+    @staticmethod
+    def ms(a, b):
+        return a.elapsed_time(b)
+
+    def destroy(self):
+        self.made = []
+
+
+def flops_fwd(w):
+    return 4.0 * w.d * w.pairs_per_head() * w.B * w.Hq
+
+
+def per_kernel_algorithmic(w):
+    """Algorithmic work per launch of each kernel: ("mfma", FLOP) or ("hbm", bytes)."""
+    pairs = w.pairs_per_head() * w.B * w.Hq
+    es = 2
+    q_bytes = w.B * w.Hq * w.Sq * w.d * es
+    kv_bytes = w.B * w.Hkv * w.Skv * w.d * es
+    lse_bytes = w.B * w.Hq * w.Sq * 4
+    out = {
+        # forward: Q K^T and P V, 2 FLOP per multiply-add each
+        "fwd_bf16_kernel": ("mfma", 4.0 * w.d * pairs),
+        # D = rowsum(dO * O): read O and dO, write D
+        "bwd_dot_do_o_kernel": ("hbm", 2.0 * q_bytes + lse_bytes),
+        # S, dP, dV and dK products (the recomputed S is one of the five
+        # backward products, so it is credited here)
+        "bwd_dkdv_kernel": ("mfma", 8.0 * w.d * pairs),
+        # dQ product only; its recomputation of S and dP is not credited
+        "bwd_dq_kernel": ("mfma", 2.0 * w.d * pairs),
+    }
+    if w.kind == "decode":
+        split_bytes = 2 * kv_bytes + q_bytes + w.n_splits * w.B * w.Hq * (w.d + 2) * 4
+        out = {"decode_split_kernel": ("hbm", float(split_bytes)),
+               "decode_combine_kernel": ("hbm", float(w.n_splits * w.B * w.Hq * (w.d + 2) * 4
+                                                      + q_bytes + w.B * w.Hq * 4))}
+    return out
+
+
+def source_hash(kernel):
+    path = os.path.join(ROOT, "attention_online_softmax_amd", "csrc", SOURCES[kernel])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "attention_online_softmax_amd", "csrc", "common.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w, cpu_inputs, budget_s=15.0):
+    """Time the oracle as it stands on whole heads of the same inputs until
+    about budget_s seconds have passed; report algorithmic TFLOP/s."""
+    import oracle
+    from attention_online_softmax_amd.inputs import to_f64
+    q, k, v, do = (cpu_inputs[n] for n in ("q", "k", "v", "do"))
+    G = w.Hq // w.Hkv
+    pairs = w.pairs_per_head()
+    done, flop = 0, 0.0
+    t0 = time.perf_counter()
+    for h in range(w.Hq):
+        kh = h // G
+        qq = to_f64(q[0:1, h:h + 1])
+        kk = to_f64(k[0:1, kh:kh + 1])
+        vv = to_f64(v[0:1, kh:kh + 1])
+        dd = to_f64(do[0:1, h:h + 1])
+        _, lse = oracle.attention_ref(qq, kk, vv, w.causal, w.scale)
+        oracle.attention_bwd_ref(qq, kk, vv, dd, w.causal, w.scale, lse=lse)
+        done += 1
+        flop += 14.0 * w.d * pairs
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward+backward on {done} of {w.B * w.Hq} heads "
+                      f"(batch 0, query heads 0..{done - 1}) of the same inputs, full "
+                      f"S={w.Sq}, {dt:.1f} s",
+            "seconds": dt}
+
+
+def quantiles(xs):
+    s = sorted(xs)
+    n = len(s)
+    return {"median": s[n // 2], "p10": s[max(0, int(0.1 * n))], "p90": s[min(n - 1, int(0.9 * n))]}
+
+
+def run_calls(calls, n_kernels, hev, steps, stream):
+    """Run `steps` iterations of the ABI calls, recording events around every
+    kernel of every call.  Returns (total ms, {call: [[ms per kernel], ...]})."""
+    import torch
+    import attention_online_softmax_amd as aos
+    per = {name: hev.create(2 * n_kernels[name] * steps) for name, _ in calls}
+    start, end = hev.create(2)
+    torch.cuda.synchronize()
+    hev.record(start, stream)
+    for s in range(steps):
+        for name, fn in calls:
+            nk = n_kernels[name]
+            aos.attn_set_timing_events(hev.handles(per[name][2 * nk * s: 2 * nk * (s + 1)]))
+            fn(s)
+    aos.attn_set_timing_events(None)
+    hev.record(end, stream)
+    torch.cuda.synchronize()
+    total = hev.ms(start, end)
+    times = {}
+    for name, _ in calls:
+        nk = n_kernels[name]
+        ev = per[name]
+        times[name] = [[hev.ms(ev[2 * nk * s + 2 * i], ev[2 * nk * s + 2 * i + 1])
+                        for i in range(nk)] for s in range(steps)]
+    return total, times
+
+
+def kernel_stats(times, name, w):
+    out = {}
+    algo = per_kernel_algorithmic(w)
+    for i, kname in enumerate(KERNELS[name]):
+        ms = [t[i] for t in times[name]]
+        avg = sum(ms) / len(ms)
+        bound, work = algo[kname]
+        rate = work / (avg * 1e-3) / (1e12 if bound == "mfma" else 1e9)
+        out[kname] = {"avg_us": avg * 1e3, **{k + "_us": v * 1e3 for k, v in quantiles(ms).items()},
+                      "bound": bound,
+                      "achieved": rate,
+                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                      "frac": rate / (PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS),
+                      "work_per_launch": work}
+    return out
+
+
+def bench_fwd_bwd(args, hev, stream):
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    w = WORKLOADS["train_fwd_bwd"]
+    cpu0 = make_workload(w)
+    sets = [{k: v.cuda() for k, v in cpu0.items()}]
+    for i in (1, 2):
+        sets.append({k: v.cuda() for k, v in make_workload(w, w.seed_base + 100 * i).items()})
+    outs = []
+    for s in sets:
+        o = torch.empty_like(s["q"])
+        lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
+        ws = torch.empty(aos.attn_bwd_workspace_bytes(w.B, w.Hq, w.Sq, w.d), device="cuda",
+                         dtype=torch.uint8)
+        outs.append(dict(o=o, lse=lse, dq=torch.empty_like(s["q"]), dk=torch.empty_like(s["k"]),
+                         dv=torch.empty_like(s["v"]), ws=ws))
+
+    def fwd(i):
+        s, o = sets[i % 3], outs[i % 3]
+        aos.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w.scale, o=o["o"], lse=o["lse"])
+
+    def bwd(i):
+        s, o = sets[i % 3], outs[i % 3]
+        aos.attn_bwd(s["q"], s["k"], s["v"], o["o"], s["do"], o["lse"], causal=True, scale=w.scale,
+                     dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["ws"])
+
+    calls = [("fwd", fwd), ("bwd", bwd)]
+    nk = {"fwd": 1, "bwd": 3}
+    for i in range(args.warmup):
+        fwd(i)
+        bwd(i)
+    torch.cuda.synchronize()
+    total_ms, times = run_calls(calls, nk, hev, args.steps, stream)
+    ks = {}
+    ks.update(kernel_stats(times, "fwd", w))
+    ks.update(kernel_stats(times, "bwd", w))
+    flop_fwd = flops_fwd(w)
+    flop_step = flop_fwd * 3.5
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(t[0] for t in times["fwd"]) / args.steps
+    bwd_ms = sum(sum(t) for t in times["bwd"]) / args.steps
+    return w, cpu0, {
+        "ms_per_step": ms_step,
+        "value": flop_step / (ms_step * 1e-3) / 1e12,
+        "fwd": {"ms": fwd_ms, "TFLOP/s": flop_fwd / (fwd_ms * 1e-3) / 1e12},
+        "bwd": {"ms": bwd_ms, "TFLOP/s": 2.5 * flop_fwd / (bwd_ms * 1e-3) / 1e12},
+        "kernels": ks,
+    }
+
+
+def bench_decode(args, hev, stream, reps):
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    w = WORKLOADS["gqa_decode"]
+    sets = [{k: v.cuda() for k, v in make_workload(w, w.seed_base + 100 * i).items()}
+            for i in range(3)]
+    ws = torch.empty(aos.attn_decode_workspace_bytes(w.B, w.Hq, w.d, w.n_splits), device="cuda",
+                     dtype=torch.uint8)
+    outs = [(torch.empty_like(s["q"]), torch.empty((w.B, w.Hq, 1), device="cuda",
+                                                   dtype=torch.float32)) for s in sets]
+
+    def dec(i):
+        s, (o, lse) = sets[i % 3], outs[i % 3]
+        aos.attn_decode(s["q"], s["k"], s["v"], scale=w.scale, n_splits=w.n_splits, o=o, lse=lse,
+                        workspace=ws)
+
+    for i in range(5):
+        dec(i)
+    total_ms, times = run_calls([("decode", dec)], {"decode": 2}, hev, reps, stream)
+    ks = kernel_stats(times, "decode", w)
+    per_call = [sum(t) for t in times["decode"]]
+    q = quantiles(per_call)
+    kv = 2.0 * w.B * w.Hkv * w.Skv * w.d * 2
+    algo = kv + 2.0 * w.B * w.Hq * w.d * 2 + w.B * w.Hq * 4
+    return {"workload": "gqa_decode: bf16, B8 Hq32 Hkv8 Skv4096 d128, 16 splits",
+            "us_median": q["median"] * 1e3, "us_p10": q["p10"] * 1e3, "us_p90": q["p90"] * 1e3,
+            "call_us_incl_gaps": total_ms / reps * 1e3,
+            "GB/s": algo / (q["median"] * 1e-3) / 1e9,
+            "frac_of_8TBs": algo / (q["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes": algo, "kernels": ks}
+
+
+def bench_prefill(args, hev, stream, reps):
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    w = WORKLOADS["long_prefill"]
+    s = {k: v.cuda() for k, v in make_workload(w).items()}
+    o = torch.empty_like(s["q"])
+    lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
+
+    def fwd(i):
+        aos.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w.scale, o=o, lse=lse)
+
+    fwd(0)
+    torch.cuda.synchronize()
+    total_ms, times = run_calls([("fwd", fwd)], {"fwd": 1}, hev, reps, stream)
+    ms = [t[0] for t in times["fwd"]]
+    q = quantiles(ms)
+    fl = flops_fwd(w)
+    return {"workload": "long_prefill: bf16 causal, B1 Hq16 Hkv2 S44032 d256",
+            "ms_median": q["median"], "ms_p10": q["p10"], "ms_p90": q["p90"],
+            "TFLOP/s": fl / (q["median"] * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (q["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", choices=["fwd_bwd", "decode", "prefill"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_online_softmax_amd as aos
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    aos.lib()
+    hev = HipEvents()
+    stream = torch.cuda.current_stream()
+
+    if args.only == "decode":
+        print(json.dumps(bench_decode(args, hev, stream, args.steps)), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps(bench_prefill(args, hev, stream, args.steps)), flush=True)
+        return
+
+    w, cpu0, r = bench_fwd_bwd(args, hev, stream)
+    print(f"[bench] fwd+bwd: {r['ms_per_step']:.3f} ms/step, {r['value']:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    extras = {}
+    if not args.no_extras and args.only is None:
+        extras["decode"] = bench_decode(args, hev, stream, max(args.steps, 50))
+        print(f"[bench] decode: {extras['decode']['us_median']:.1f} us", file=sys.stderr,
+              flush=True)
+        extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
+        print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",
+              file=sys.stderr, flush=True)
+
+    ks = r["kernels"]
+    dom = max(ks, key=lambda k: ks[k]["avg_us"])
+    d = ks[dom]
+    traffic = stored_traffic(dom, w.key)
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+                "peak": PEAK_BF16_TFLOPS if d["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": d["unit"], "frac": d["frac"], "traffic": traffic,
+                "avg_us": d["avg_us"], "work_per_launch": d["work_per_launch"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, cpu0)
+        print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "train_fwd_bwd: attn_fwd + attn_bwd, bf16 storage, fp32 "
+                               "accumulate, causal, B4 H16 S2048 d128",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Sq, "head_dim": w.d,
+                   "causal": True, "parallelism": "single GPU"},
+        "frac_of_bf16_peak": r["value"] / PEAK_BF16_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fwd": r["fwd"],
+        "bwd": r["bwd"],
+        "kernels": ks,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+    hev.destroy()
+
+
+if __name__ == "__main__":
+    main()
