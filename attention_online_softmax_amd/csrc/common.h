@@ -49,6 +49,45 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // Lane exchange with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// max(x, x of the lane 32 away) and x + (x of the lane 32 away), using the
+// VALU half-wave swap: after the swap one register holds the low half-wave's
+// values in both halves and the other the high half-wave's, so the
+// combination is the same in every lane.
+__device__ __forceinline__ float halfwave_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane L supplies the address of 4 consecutive bf16 that form row L/4,
+// columns 4*(L%4) .. 4*(L%4)+3 of a 4 x 16 block; lane j receives column j
+// of that block (its 4 rows, in row order).
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uint16_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Per-lane offset (in elements) for tr_col8 within a row-major LDS tile of
+// the given pitch.
+__device__ __forceinline__ int tr_lane_offset(int lane, int pitch) {
+  return ((lane >> 2) & 3) * pitch + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
+// k-operand of a 32x32x16 MFMA contracted over 8 consecutive ROWS of a
+// row-major LDS tile: lane l gets rows r0 .. r0+7 (r0 = base + 8*(l/32),
+// uniform per 16-lane group) of column c0 + l%32.  `p` = tile + r0*pitch +
+// c0 + tr_lane_offset(lane, pitch).
+__device__ __forceinline__ u32x4 tr_col8(const uint16_t* p, int pitch) {
+  const u32x2 a = lds_tr4(p);
+  const u32x2 b = lds_tr4(p + 4 * pitch);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -121,43 +121,76 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // Four waves per workgroup, 32 query rows per wave.  Scores are formed
 // transposed, S^T = K Q^T (A = key rows from LDS, B = the wave's queries held
 // in registers), so each lane owns ONE query column and 16 of its scores per
-// 32-key block: the row maximum and row sum are lane-local plus one exchange
-// with the other half-wave.  Key rows are fed to the MFMA in swap23 order so
-// that the probabilities a lane holds are 8 contiguous keys, which is exactly
-// the B-operand layout of O^T += V^T P^T; the accumulator O^T is again
-// indexed by the lane's query, so the rescale by alpha is a per-lane scalar.
+// 32-key block: the row maximum and row sum are lane-local plus one half-wave
+// swap.  Key rows are fed to the MFMA in swap23 order so that the
+// probabilities a lane holds are 8 contiguous keys, which is exactly the
+// B-operand layout of O^T += V^T P^T; V^T comes straight from the row-major
+// V tile through LDS transpose reads.  The accumulator O^T is again indexed
+// by the lane's query, so rescaling by alpha is a per-lane scalar.
+//
+// K/V tiles go from HBM straight into LDS with global_load_lds (no staging
+// registers), double-buffered: tile j+1 is in flight while tile j is used.
+// Tiles are dense [BC][D] with 16-byte chunks XOR-swizzled per row so that
+// both the K row reads and the V transpose reads hit 32 distinct banks.
+//
+// Normalisation reference: the exponentials are taken relative to a per-row
+// reference m_ref that only advances when the row maximum exceeds it by more
+// than kLazy (log2 units); o and l are rescaled only then.  o, l and m_ref
+// always describe the same partial softmax (o and l relative to exp2(m_ref)),
+// so O = o / l and LSE = m_ref + log2 l are unchanged in exact arithmetic,
+// and probabilities stay below 2^kLazy.
 // ---------------------------------------------------------------------------
+constexpr float kLazy = 8.f;
+
 template <int D>
 struct FwdTile {
-  static constexpr int BC = (D >= 256) ? 32 : 64;  // keys per LDS tile
-  static constexpr int PITCH = D + 8;              // LDS row pitch in bf16 (16-byte pad)
+  static constexpr int BC = 64;                   // keys per LDS tile
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int DMA = BC * D / 512;        // 1 KB DMA blocks per tensor per tile
+  static constexpr int DMA_PER_WAVE = DMA / 4;
 };
 
-// V^T operand: 8 contiguous keys starting at key row `r0` of the LDS tile,
-// column `col`, packed as 8 bf16.
-__device__ __forceinline__ u32x4 gather_col8(const uint16_t* s, int r0, int col, int pitch) {
-  const uint16_t* p = s + r0 * pitch + col;
-  u32x4 r;
+// Physical 16-byte chunk of logical chunk `c` in row `r`.
+// K: XOR with swap23(r) & 7 (the rows a group of 8 lanes reads together in
+// swap23 order then use 8 distinct chunk positions of a 128-byte window).
+// V: XOR with 2 (r & 3) (the 4 rows of one transpose read use 4 distinct
+// 32-byte windows).
+__device__ __forceinline__ int k_swz(int r) { return swap23(r) & 7; }
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+
+// Issue this wave's share of the DMA for a [BC][D] tile starting at key k0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int k0, int Skv,
+                                         int wave, int lane) {
+  constexpr int CPR = FwdTile<D>::CPR;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = uint32_t(p[(2 * j) * pitch]) | (uint32_t(p[(2 * j + 1) * pitch]) << 16);
+  for (int j = 0; j < FwdTile<D>::DMA_PER_WAVE; ++j) {
+    const int blk = j * 4 + wave;
+    const int pos = blk * 64 + lane;             // physical chunk index in the tile
+    const int r = pos / CPR;
+    const int pc = pos % CPR;
+    const int lc = pc ^ (IS_V ? v_swz(r) : k_swz(r));
+    const int key = min(k0 + r, Skv - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * D + lc * 8),
+                                     (__attribute__((address_space(3))) void*)(dst + blk * 512),
+                                     16, 0, 0);
   }
-  return r;
 }
 
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, int n_qtiles) {
   constexpr int BR = 128;
   constexpr int BC = FwdTile<D>::BC;
-  constexpr int PITCH = FwdTile<D>::PITCH;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BC * PITCH];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -168,17 +201,32 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
   const int off = Skv - Sq;
-  const int row = qtile * BR + wave * 32 + n;
+  const int wave_row0 = qtile * BR + wave * 32;
+  const int row = wave_row0 + n;
   const bool valid = row < Sq;
 
   const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
 
+  const int last_row = min(qtile * BR + BR, Sq) - 1;
+  const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  // Start the first tile's transfer before anything else.
+  dma_tile<D, false>(Kh, sK[0], 0, Skv, wave, lane);
+  dma_tile<D, true>(Vh, sV[0], 0, Skv, wave, lane);
+
+  // A negative scale is applied as |scale| on -Q (bf16 negation is exact),
+  // so the maximum can be taken on raw scores and scaled afterwards.
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c2 = fabsf(scale_log2);
   u32x4 qreg[NDC];
+  const int qrow = min(row, Sq - 1);
 #pragma unroll
   for (int c = 0; c < NDC; ++c) {
-    qreg[c] = valid ? *(const u32x4*)(Qh + (int64_t)row * D + c * 16 + 8 * g) : u32x4{0, 0, 0, 0};
+    qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
+    qreg[c] ^= qsign;
   }
   f32x16 oacc[NDB];
 #pragma unroll
@@ -186,62 +234,65 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
-  const int last_row = min(qtile * BR + BR, Sq) - 1;
-  const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
-  const int first_row = qtile * BR;
+  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [0, row_limit)
+  // Last key any row of this wave may see (tiles beyond it are skipped).
+  const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
 
-  float m = kNegInf, lpart = 0.f;
-  for (int k0 = 0; k0 < kv_end; k0 += BC) {
-    __syncthreads();
-    for (int e = tid * 8; e < BC * D; e += 256 * 8) {
-      const int r = e / D, c = e % D;
-      const int key = k0 + r;
-      u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (key < Skv) {
-        kx = *(const u32x4*)(Kh + (int64_t)key * D + c);
-        vx = *(const u32x4*)(Vh + (int64_t)key * D + c);
-      }
-      *(u32x4*)(sK + r * PITCH + c) = kx;
-      *(u32x4*)(sV + r * PITCH + c) = vx;
-    }
-    __syncthreads();
+  // Per-lane LDS offsets (elements).  K row reads: row kb*32 + swap23(n),
+  // logical chunk 2c + g, physical chunk (2c + g) ^ (n & 7).
+  const int k_row = swap23(n) * D;
+  int k_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_off[c] = k_row + 8 * ((2 * c + g) ^ (n & 7));
+  // V transpose reads: row r0 + (lane>>2)&3 with r0 = 32kb + 16c + 8g (+4),
+  // logical chunk 4db + 2((lane>>4)&1) + ((lane>>1)&1), element (lane&1)*4,
+  // physical chunk = logical ^ 2((lane>>2)&3).
+  const int vr = (lane >> 2) & 3;
+  const int v_lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  int v_off[2];
+#pragma unroll
+  for (int dbp = 0; dbp < 2; ++dbp)
+    v_off[dbp] = (8 * g + vr) * D + 8 * ((4 * dbp + v_lc) ^ (2 * vr)) + 4 * (lane & 1);
 
+  float m_ref = kNegInf, lpart = 0.f;
+
+  auto tile = [&](const uint16_t* cK, const uint16_t* cV, int k0, bool need_mask) {
     f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* krow = sK + (kb * 32 + swap23(n)) * PITCH + 8 * g;
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        s[kb] = mfma32(*(const u32x4*)(krow + c * 16), qreg[c], s[kb]);
-      }
-    }
-    // Keys this tile can mask: causal diagonal or the ragged end of Skv.
-    const bool need_mask = (k0 + BC > Skv) || (CAUSAL && k0 + BC - 1 > first_row + off);
-    float mx = m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * scale_log2;
-        if (need_mask) {
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma32(*(const u32x4*)(cK + kb * 32 * D + k_off[c & 3] + 64 * (c >> 2)),
+                       qreg[c], s[kb]);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= row_limit) x = kNegInf;
+          s[kb][i] = (key < row_limit) ? s[kb][i] : kNegInf;
         }
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float msub = (mx == kNegInf) ? 0.f : mx;
-    const float alpha = fast_exp2(m - msub);
-    lpart *= alpha;
+    }
+    float rmax = kNegInf;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
+      for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[kb][i]);
+    const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
+    if (__any(mnew > m_ref + kLazy)) {
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_ref = mnew;
+    }
+    const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
     u32x4 pb[NKB][2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -249,24 +300,39 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(s[kb][8 * c + 2 * j] - msub);
-          const float p1 = fast_exp2(s[kb][8 * c + 2 * j + 1] - msub);
+          const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2, -msub));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2, -msub));
           lpart += p0 + p1;
           pb[kb][c][j] = pack_bf16x2(p0, p1);
         }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4 a = gather_col8(sV, kb * 32 + 16 * c + 8 * g, db * 32 + n, PITCH);
-          oacc[db] = mfma32(a, pb[kb][c], oacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const uint16_t* vp = cV + (kb * 32 + 16 * c) * D + v_off[db & 1] + 64 * (db >> 1);
+          oacc[db] = mfma32(tr_col8(vp, D), pb[kb][c], oacc[db]);
         }
-    m = mx;
+  };
+
+#pragma clang loop unroll(disable)
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    const int k0 = tt * BC;
+    const int buf = tt & 1;
+    wait_vmcnt0();      // this wave's part of tile tt has landed in LDS
+    __syncthreads();    // ... and every wave's; tile tt-1's buffer is free
+    if (tt + 1 < n_tiles) {
+      dma_tile<D, false>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, true>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
+    }
+    if (k0 <= wave_kv_last) {
+      const bool need_mask = (k0 + BC > Skv) || (CAUSAL && k0 + BC - 1 > wave_row0 + off);
+      tile(sK[buf], sV[buf], k0, need_mask);
+    }
   }
 
-  const float l = lpart + xor32(lpart);
+  const float l = halfwave_sum(lpart);
   if (!valid) return;
   const float inv = 1.f / l;
   uint16_t* Orow = O + ((int64_t)bh * Sq + row) * D;
@@ -279,7 +345,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
                  pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv)};
       *(u32x2*)(Orow + d0) = w;
     }
-  if (LSE && g == 0) LSE[(int64_t)bh * Sq + row] = (m + fast_log2(l)) * kLn2;
+  if (LSE && g == 0) LSE[(int64_t)bh * Sq + row] = (m_ref + fast_log2(l)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
