@@ -8,21 +8,26 @@
 // With P = exp(scale Q K^T + C - LSE):
 //   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// Three kernels: D per query row; dK and dV per key tile (looping over the
-// query tiles and the query heads of a grouped key/value head, so every
-// dK/dV element is written once); dQ per query tile.  No atomics.
+// Three kernels: per query row D and -LSE log2(e); dK and dV per key tile
+// (looping over the query tiles and the query heads of a grouped key/value
+// head, so every dK/dV element is written once); dQ per query tile.  No
+// atomics.  Both product kernels stream their tiles HBM -> LDS with
+// global_load_lds into double-buffered, swizzled tiles (see common.h) that
+// are read both by rows and, through transpose reads, by columns.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO[i, c] * O[i, c] in fp32 (bf16 inputs).
+// Per query row: D_i = sum_c dO[i, c] * O[i, c] and nl_i = -LSE_i * log2(e),
+// both fp32, written to the workspace as [D (rows)] [nl (rows)].
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
-                                                           float* __restrict__ Dd, int64_t rows) {
+                                                           const float* __restrict__ LSE,
+                                                           float* __restrict__ ws, int64_t rows) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -39,24 +44,10 @@ __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __res
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
-  if (row < rows && sub == 0) Dd[row] = acc;
-}
-
-template <int D>
-struct BwdTile {
-  static constexpr int PITCH = D + 8;  // LDS row pitch in bf16
-};
-
-// 8 contiguous rows r0 .. r0+7 of column `col` of a row-major LDS tile,
-// packed as 8 bf16: the k-operand of a product contracted over those rows.
-__device__ __forceinline__ u32x4 bwd_col8(const uint16_t* s, int r0, int col, int pitch) {
-  const uint16_t* p = s + r0 * pitch + col;
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = uint32_t(p[(2 * j) * pitch]) | (uint32_t(p[(2 * j + 1) * pitch]) << 16);
+  if (row < rows && sub == 0) {
+    ws[row] = acc;
+    ws[rows + row] = -LSE[row] * kLog2e;
   }
-  return r;
 }
 
 // Transposed accumulator X^T[d][row] (lane = row n, 16 d values per 32-d
@@ -77,45 +68,79 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (b, key/value head, 128-key tile); each of its
-// four waves owns 32 keys, holding their K and V rows in registers and their
-// dK^T, dV^T accumulators.  Query tiles of 32 rows (Q, dO, LSE, D) are staged
-// through LDS.  Scores are formed S = Q K^T with query rows fed in swap23
-// order, so each lane (one key) holds P for 8 contiguous queries per k-step:
-// the B operand of dV^T += dO^T P and dK^T += Q^T dS.
+// four waves owns 32 keys, holding their K and V rows in registers (the
+// B operands of S = Q K^T and dP = dO V^T) and their dK^T, dV^T accumulators.
+// Query tiles of 64 rows of Q and dO, plus D and nl for those rows, stream
+// through LDS.  Per 32-query sub-block, Q and dO rows are fed to the MFMA in
+// swap23 order, so each lane (one key) holds P and dS for 8 contiguous
+// queries per k-step: the B operands of dV^T += dO^T P and dK^T += Q^T dS,
+// whose A operands dO^T and Q^T come from transpose reads of the same tiles.
 // ---------------------------------------------------------------------------
+template <int D>
+struct BwdTile {
+  static constexpr int QB = 64;   // query rows per LDS tile (dK/dV)
+  static constexpr int KB = 64;   // key rows per LDS tile (dQ)
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Skv,
-    float scale, float scale_log2, int n_ktiles) {
-  constexpr int QB = 32;
-  constexpr int PITCH = BwdTile<D>::PITCH;
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Skv, float scale,
+    float scale_log2, int64_t rows_total) {
+  constexpr int QB = BwdTile<D>::QB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[QB * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[QB * PITCH];
-  __shared__ float sL[QB];
-  __shared__ float sD[QB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][QB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG[2][QB * D];
+  __shared__ __attribute__((aligned(16))) float sDn[2][2 * QB];   // D then nl
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-  const int bhk = blockIdx.x % (gridDim.x / n_ktiles);
-  const int ktile = blockIdx.x / (gridDim.x / n_ktiles);
+  const int bhk = blockIdx.x % BHk;
+  const int ktile = blockIdx.x / BHk;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int G = Hq / Hkv;
   const int off = Skv - Sq;
-  const int key = ktile * 128 + wave * 32 + n;
+  const int key0_wave = ktile * 128 + wave * 32;
+  const int key = key0_wave + n;
   const bool kvalid = key < Skv;
 
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
+  const float* Dd = ws;
+  const float* NL = ws + rows_total;
+
+  // Queries that can see any key of this tile: i >= first_key - off.
+  const int q_begin = CAUSAL ? max(0, ktile * 128 - off) : 0;
+  const int q_start = (q_begin / QB) * QB;
+  const int n_qt = (Sq - q_start + QB - 1) / QB;  // query tiles per head
+  const int n_it = G * n_qt;
+
+  auto issue = [&](int it, int buf) {
+    const int hh = it / n_qt;
+    const int q0 = q_start + (it % n_qt) * QB;
+    const int64_t bh = (int64_t)b * Hq + hk * G + hh;
+    dma_tile<D, QB, 4>(Q + bh * Sq * D, sQ[buf], q0, Sq, wave, lane);
+    dma_tile<D, QB, 4>(dO + bh * Sq * D, sG[buf], q0, Sq, wave, lane);
+    if (wave < 2) {
+      // wave 0: D of rows q0 .. q0+63, wave 1: nl of those rows, one float
+      // per lane (rows past Sq repeat row Sq-1; they are masked).
+      const float* src = (wave == 0 ? Dd : NL) + bh * Sq + min(q0 + lane, Sq - 1);
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)&sDn[buf][wave * QB],
+                                       4, 0, 0);
+    }
+  };
+  issue(0, 0);
+
   u32x4 kreg[NDC], vreg[NDC];
+  const int krow = min(key, Skv - 1);
 #pragma unroll
   for (int c = 0; c < NDC; ++c) {
-    kreg[c] = kvalid ? *(const u32x4*)(Kh + (int64_t)key * D + c * 16 + 8 * g) : u32x4{0, 0, 0, 0};
-    vreg[c] = kvalid ? *(const u32x4*)(Vh + (int64_t)key * D + c * 16 + 8 * g) : u32x4{0, 0, 0, 0};
+    kreg[c] = *(const u32x4*)(Kh + (int64_t)krow * D + c * 16 + 8 * g);
+    vreg[c] = *(const u32x4*)(Vh + (int64_t)krow * D + c * 16 + 8 * g);
   }
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -123,103 +148,104 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkt[db][i] = dvt[db][i] = 0.f;
 
-  // Queries that can see any key of this tile: i >= first_key - off.
-  const int first_key = ktile * 128;
-  const int q_begin = CAUSAL ? max(0, first_key - off) : 0;
-  const int q_start = (q_begin / QB) * QB;
+  int r_off[4], t_off[2];
+  row_read_offsets<D>(n, g, r_off);
+  tr_read_offsets<D>(lane, t_off);
 
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = hk * G + hh;
-    const int64_t bh = (int64_t)b * Hq + h;
-    const uint16_t* Qh = Q + bh * Sq * D;
-    const uint16_t* dOh = dO + bh * Sq * D;
-    for (int q0 = q_start; q0 < Sq; q0 += QB) {
-      __syncthreads();
-      for (int e = tid * 8; e < QB * D; e += 256 * 8) {
-        const int r = e / D, c = e % D;
-        const int qi = q0 + r;
-        u32x4 qx = {0, 0, 0, 0}, gx = {0, 0, 0, 0};
-        if (qi < Sq) {
-          qx = *(const u32x4*)(Qh + (int64_t)qi * D + c);
-          gx = *(const u32x4*)(dOh + (int64_t)qi * D + c);
-        }
-        *(u32x4*)(sQ + r * PITCH + c) = qx;
-        *(u32x4*)(sdO + r * PITCH + c) = gx;
-      }
-      if (tid < QB) {
-        const int qi = q0 + tid;
-        sL[tid] = (qi < Sq) ? LSE[bh * Sq + qi] * kLog2e : 0.f;
-        sD[tid] = (qi < Sq) ? Dd[bh * Sq + qi] : 0.f;
-      }
-      __syncthreads();
-
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
+#pragma clang loop unroll(disable)
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    const int q0 = q_start + (it % n_qt) * QB;
+    wait_vmcnt0();
+    __syncthreads();
+    if (it + 1 < n_it) issue(it + 1, buf ^ 1);
+    const uint16_t* cQ = sQ[buf];
+    const uint16_t* cG = sG[buf];
+#pragma unroll
+    for (int sb = 0; sb < QB / 32; ++sb) {
+      const int qs = q0 + sb * 32;
+      // Sub-block fully hidden from this wave's keys: skip.
+      if (CAUSAL && key0_wave > qs + 31 + off) continue;
+      if (qs >= Sq) continue;
+      // Queries past Sq read a repeated row and must not contribute; keys
+      // past Skv only affect their own (unstored) dK/dV columns.
+      const bool need_mask = (qs + 32 > Sq) || (CAUSAL && key0_wave + 31 > qs + off);
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      const uint16_t* qrow = sQ + swap23(n) * PITCH + 8 * g;
-      const uint16_t* grow = sdO + swap23(n) * PITCH + 8 * g;
+      const uint16_t* qb = cQ + sb * 32 * D;
+      const uint16_t* gb = cG + sb * 32 * D;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        s = mfma32(*(const u32x4*)(qrow + c * 16), kreg[c], s);
-        dp = mfma32(*(const u32x4*)(grow + c * 16), vreg[c], dp);
+        const int o = r_off[c & 3] + 64 * (c >> 2);
+        s = mfma32(*(const u32x4*)(qb + o), kreg[c], s);
+        dp = mfma32(*(const u32x4*)(gb + o), vreg[c], dp);
       }
-      // Element i is query q0 + 16*(i/8) + 8g + i%8 against key `key`.
+      // Element i is query qs + 16*(i/8) + 8g + i%8 against key `key`.
+      const float* dn = &sDn[buf][sb * 32];
       u32x4 pb[2], dsb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const f32x4 d0 = *(const f32x4*)(dn + 16 * c + 8 * g);
+        const f32x4 d1 = *(const f32x4*)(dn + 16 * c + 8 * g + 4);
+        const f32x4 l0 = *(const f32x4*)(dn + QB + 16 * c + 8 * g);
+        const f32x4 l1 = *(const f32x4*)(dn + QB + 16 * c + 8 * g + 4);
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * c + j;
+          const float nl = j < 4 ? l0[j] : l1[j - 4];
+          const float dd = j < 4 ? d0[j] : d1[j - 4];
+          float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+          if (need_mask) {
+            const int qi = qs + 16 * c + 8 * g + j;
+            const bool ok = (qi < Sq) && (!CAUSAL || key <= qi + off);
+            p = ok ? p : 0.f;
+          }
+          pv[j] = p;
+          dsv[j] = p * (dp[i] - dd);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pb[c][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+          dsb[c][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (contracted over the 32 queries).
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float pv[2], dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 8 * c + 2 * j + u;
-            const int ql = 16 * c + 8 * g + 2 * j + u;
-            const int qi = q0 + ql;
-            bool ok = (qi < Sq) && kvalid;
-            if (CAUSAL) ok = ok && (key <= qi + off);
-            const float p = ok ? fast_exp2(s[i] * scale_log2 - sL[ql]) : 0.f;
-            pv[u] = p;
-            dsv[u] = p * (dp[i] - sD[ql]);
-          }
-          pb[c][j] = pack_bf16x2(pv[0], pv[1]);
-          dsb[c][j] = pack_bf16x2(dsv[0], dsv[1]);
-        }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (contracted over the 32 queries).
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          dvt[db] = mfma32(bwd_col8(sdO, 16 * c + 8 * g, db * 32 + n, PITCH), pb[c], dvt[db]);
-          dkt[db] = mfma32(bwd_col8(sQ, 16 * c + 8 * g, db * 32 + n, PITCH), dsb[c], dkt[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const int o = 16 * c * D + t_off[db & 1] + 64 * (db >> 1);
+          dvt[db] = mfma32(tr_col8(gb + o, D), pb[c], dvt[db]);
+          dkt[db] = mfma32(tr_col8(qb + o, D), dsb[c], dkt[db]);
         }
     }
   }
   if (!kvalid) return;
-  const int64_t krow = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
-  store_transposed<NDB>(dK + krow, dkt, g, scale);
-  store_transposed<NDB>(dV + krow, dvt, g, 1.f);
+  const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
+  store_transposed<NDB>(dK + kro, dkt, g, scale);
+  store_transposed<NDB>(dV + kro, dvt, g, 1.f);
 }
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, query head, 128-query tile), 32 queries per wave
 // with their Q and dO rows in registers.  Key tiles of 64 rows (K and V)
-// are staged in LDS.  Scores are formed transposed, S^T = K Q^T, so the lane
-// (one query) holds dS^T for 8 contiguous keys per k-step: the B operand of
-// dQ^T += K^T dS^T.
+// stream through LDS.  Scores are formed transposed, S^T = K Q^T, so each
+// lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
+// of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
-    uint16_t* __restrict__ dQ, int BH, int Hq, int Hkv, int Sq, int Skv, float scale,
-    float scale_log2, int n_qtiles) {
-  constexpr int BC = 64;
-  constexpr int PITCH = BwdTile<D>::PITCH;
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dQ,
+    int BH, int Hq, int Hkv, int Sq, int Skv, float scale, float scale_log2, int n_qtiles,
+    int64_t rows_total) {
+  constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BC * PITCH];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -230,21 +256,30 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
   const int off = Skv - Sq;
-  const int row = qtile * 128 + wave * 32 + n;
+  const int wave_row0 = qtile * 128 + wave * 32;
+  const int row = wave_row0 + n;
   const bool valid = row < Sq;
 
-  const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
-  const uint16_t* dOh = dO + (int64_t)bh * Sq * D;
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
+  const int last_row = min(qtile * 128 + 128, Sq) - 1;
+  const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  dma_tile<D, BC, 4>(Kh, sK[0], 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Vh, sV[0], 0, Skv, wave, lane);
+
+  const int qrow = min(row, Sq - 1);
+  const uint16_t* Qr = Q + ((int64_t)bh * Sq + qrow) * D;
+  const uint16_t* dOr = dO + ((int64_t)bh * Sq + qrow) * D;
   u32x4 qreg[NDC], greg[NDC];
 #pragma unroll
   for (int c = 0; c < NDC; ++c) {
-    qreg[c] = valid ? *(const u32x4*)(Qh + (int64_t)row * D + c * 16 + 8 * g) : u32x4{0, 0, 0, 0};
-    greg[c] = valid ? *(const u32x4*)(dOh + (int64_t)row * D + c * 16 + 8 * g) : u32x4{0, 0, 0, 0};
+    qreg[c] = *(const u32x4*)(Qr + c * 16 + 8 * g);
+    greg[c] = *(const u32x4*)(dOr + c * 16 + 8 * g);
   }
-  const float lse2 = valid ? LSE[(int64_t)bh * Sq + row] * kLog2e : 0.f;
-  const float dd = valid ? Dd[(int64_t)bh * Sq + row] : 0.f;
+  const float dd = ws[(int64_t)bh * Sq + qrow];
+  const float nl = ws[rows_total + (int64_t)bh * Sq + qrow];
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -252,34 +287,38 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     for (int i = 0; i < 16; ++i) dqt[db][i] = 0.f;
 
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
-  const int last_row = min(qtile * 128 + 128, Sq) - 1;
-  const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
+  const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
+  int r_off[4], t_off[2];
+  row_read_offsets<D>(n, g, r_off);
+  tr_read_offsets<D>(lane, t_off);
 
-  for (int k0 = 0; k0 < kv_end; k0 += BC) {
+#pragma clang loop unroll(disable)
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    const int k0 = tt * BC;
+    const int buf = tt & 1;
+    wait_vmcnt0();
     __syncthreads();
-    for (int e = tid * 8; e < BC * D; e += 256 * 8) {
-      const int r = e / D, c = e % D;
-      const int kk = k0 + r;
-      u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (kk < Skv) {
-        kx = *(const u32x4*)(Kh + (int64_t)kk * D + c);
-        vx = *(const u32x4*)(Vh + (int64_t)kk * D + c);
-      }
-      *(u32x4*)(sK + r * PITCH + c) = kx;
-      *(u32x4*)(sV + r * PITCH + c) = vx;
+    if (tt + 1 < n_tiles) {
+      dma_tile<D, BC, 4>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
     }
-    __syncthreads();
+    const uint16_t* cK = sK[buf];
+    const uint16_t* cV = sV[buf];
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
+      const int ks = k0 + kb * 32;
+      if (ks > wave_kv_last) continue;
+      const bool need_mask = (ks + 32 > Skv) || (CAUSAL && ks + 31 > wave_row0 + off);
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      const uint16_t* krow = sK + (kb * 32 + swap23(n)) * PITCH + 8 * g;
-      const uint16_t* vrow = sV + (kb * 32 + swap23(n)) * PITCH + 8 * g;
+      const uint16_t* kbp = cK + kb * 32 * D;
+      const uint16_t* vbp = cV + kb * 32 * D;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        s = mfma32(*(const u32x4*)(krow + c * 16), qreg[c], s);
-        dp = mfma32(*(const u32x4*)(vrow + c * 16), greg[c], dp);
+        const int o = r_off[c & 3] + 64 * (c >> 2);
+        s = mfma32(*(const u32x4*)(kbp + o), qreg[c], s);
+        dp = mfma32(*(const u32x4*)(vbp + o), greg[c], dp);
       }
       u32x4 dsb[2];
 #pragma unroll
@@ -290,18 +329,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int i = 8 * c + 2 * j + u;
-            const int kk = k0 + kb * 32 + 16 * c + 8 * g + 2 * j + u;
-            const float p = (kk < row_limit) ? fast_exp2(s[i] * scale_log2 - lse2) : 0.f;
+            float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+            if (need_mask) {
+              const int kk = ks + 16 * c + 8 * g + 2 * j + u;
+              p = (kk < row_limit) ? p : 0.f;
+            }
             dsv[u] = p * (dp[i] - dd);
           }
           dsb[c][j] = pack_bf16x2(dsv[0], dsv[1]);
         }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          dqt[db] = mfma32(bwd_col8(sK, kb * 32 + 16 * c + 8 * g, db * 32 + n, PITCH), dsb[c],
-                           dqt[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const int o = 16 * c * D + t_off[db & 1] + 64 * (db >> 1);
+          dqt[db] = mfma32(tr_col8(kbp + o, D), dsb[c], dqt[db]);
+        }
     }
   }
   if (!valid) return;
@@ -314,17 +357,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
   timing_mark(a.stream, 0);
   hipLaunchKernelGGL((bwd_dot_do_o_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.ws, rows);
+                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, rows);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const int n_ktiles = (a.Skv + 127) / 128;
+  const int BHk = a.B * a.Hkv;
   timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * a.B * a.Hkv), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.d_o, a.lse, (const float*)a.ws, (uint16_t*)a.dk,
-                     (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, n_ktiles);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     BHk, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, rows);
   timing_mark(a.stream, 3);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -333,8 +377,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   timing_mark(a.stream, 4);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.d_o, a.lse, (const float*)a.ws, (uint16_t*)a.dq, BH,
-                     a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, n_qtiles);
+                     (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dq, BH, a.Hq, a.Hkv,
+                     a.Sq, a.Skv, a.scale, sl2, n_qtiles, rows);
   timing_mark(a.stream, 5);
   return hipGetLastError();
 }

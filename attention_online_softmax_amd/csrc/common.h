@@ -46,6 +46,17 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Row index of accumulator element i for a lane in half-wave g (32x32 tile).
+__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Swap bits 2 and 3 of a row index within a 32-row block.  Feeding MFMA row r
+// from physical row swap23(r) makes the eight accumulator rows a lane holds
+// for i = 8c .. 8c+7 the contiguous physical rows 16c + 8g .. 16c + 8g + 7,
+// so a score tile can be used directly as the k-operand of the next product.
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~0xc) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
 // Lane exchange with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -88,18 +99,71 @@ __device__ __forceinline__ u32x4 tr_col8(const uint16_t* p, int pitch) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled [ROWS][D] bf16 tiles in LDS, filled by global_load_lds.
+//
+// Rows are dense (D * 2 bytes); within each aligned group of eight 16-byte
+// chunks, logical chunk c of row r is stored at chunk c ^ tile_swz(r) with
+// tile_swz(r) = 2 (r & 3) | ((r >> 3) & 1).  LDS has 32 banks of 4 bytes
+// (128 bytes per cycle), so:
+//  * a b128 row read where lanes 0..7 take rows swap23(0..7) =
+//    {0,1,2,3,8,9,10,11} (plus a multiple of 32) at one logical chunk hits 8
+//    distinct chunk positions of a 128-byte window;
+//  * a transpose read where 16 lanes take 4 consecutive rows (starting at a
+//    multiple of 4) x 32 bytes hits 4 distinct 32-byte windows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile_swz(int r) { return (2 * (r & 3)) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
+// This wave's share of the transfer of rows r0 .. r0+ROWS-1 of a row-major
+// [*, D] bf16 matrix (rows at or beyond rlimit read row rlimit-1 instead)
+// into the swizzled tile `dst`.  Each global_load_lds moves 64 chunks of 16
+// bytes: lane l of block blk fills physical chunk blk*64 + l.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int r0, int rlimit,
+                                         int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int BLOCKS = ROWS * D / 512;
+  static_assert(BLOCKS % NWAVES == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < BLOCKS / NWAVES; ++j) {
+    const int blk = j * NWAVES + wave;
+    const int pos = blk * 64 + lane;
+    const int r = pos / CPR;
+    const int lc = (pos % CPR) ^ tile_swz(r);
+    const int row = min(r0 + r, rlimit - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * D + lc * 8),
+                                     (__attribute__((address_space(3))) void*)(dst + blk * 512),
+                                     16, 0, 0);
+  }
+}
+
+// Element offsets, within a swizzled [*, D] tile, of the b128 row read that
+// feeds MFMA A-row n of a 32-row block (physical row swap23(n)) with logical
+// chunk 2c + g, for c = 0..3; chunk c >= 4 adds 64 * (c / 4) elements.
+template <int D>
+__device__ __forceinline__ void row_read_offsets(int n, int g, int* off) {
+  const int h = (2 * (n & 3)) | ((n >> 2) & 1);  // tile_swz(swap23(n))
+#pragma unroll
+  for (int c = 0; c < 4; ++c) off[c] = swap23(n) * D + 8 * ((2 * c + g) ^ h);
+}
+
+// Element offsets for tr_col8 on a swizzled [*, D] tile when the 8-row group
+// starts at a row base + 8g (base a multiple of 16): logical column block
+// db (32 columns) with db even (off[0]) or odd (off[1]); block db adds
+// 64 * (db / 2) elements.
+template <int D>
+__device__ __forceinline__ void tr_read_offsets(int lane, int* off) {
+  const int g = lane >> 5;
+  const int vr = (lane >> 2) & 3;
+  const int h = (2 * vr) | g;
+  const int lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) off[p] = (8 * g + vr) * D + 8 * ((4 * p + lc) ^ h) + 4 * (lane & 1);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// Row index of accumulator element i for a lane in half-wave g (32x32 tile).
-__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
-
-// Swap bits 2 and 3 of a row index within a 32-row block.  Feeding MFMA row r
-// from physical row swap23(r) makes the eight accumulator rows a lane holds
-// for i = 8c .. 8c+7 the contiguous physical rows 16c + 8g .. 16c + 8g + 7,
-// so a score tile can be used directly as the k-operand of the next product.
-__device__ __forceinline__ int swap23(int r) {
-  return (r & ~0xc) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
 
 }  // namespace attn

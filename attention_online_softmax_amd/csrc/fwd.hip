@@ -130,8 +130,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 //
 // K/V tiles go from HBM straight into LDS with global_load_lds (no staging
 // registers), double-buffered: tile j+1 is in flight while tile j is used.
-// Tiles are dense [BC][D] with 16-byte chunks XOR-swizzled per row so that
-// both the K row reads and the V transpose reads hit 32 distinct banks.
+// Tiles are dense [BC][D] with 16-byte chunks XOR-swizzled per row
+// (tile_swz) so that the K row reads and the V transpose reads are free of
+// bank conflicts.
 //
 // Normalisation reference: the exponentials are taken relative to a per-row
 // reference m_ref that only advances when the row maximum exceeds it by more
@@ -144,40 +145,8 @@ constexpr float kLazy = 8.f;
 
 template <int D>
 struct FwdTile {
-  static constexpr int BC = 64;                   // keys per LDS tile
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int DMA = BC * D / 512;        // 1 KB DMA blocks per tensor per tile
-  static constexpr int DMA_PER_WAVE = DMA / 4;
+  static constexpr int BC = 64;  // keys per LDS tile
 };
-
-// Physical 16-byte chunk of logical chunk `c` in row `r`.
-// K: XOR with swap23(r) & 7 (the rows a group of 8 lanes reads together in
-// swap23 order then use 8 distinct chunk positions of a 128-byte window).
-// V: XOR with 2 (r & 3) (the 4 rows of one transpose read use 4 distinct
-// 32-byte windows).
-__device__ __forceinline__ int k_swz(int r) { return swap23(r) & 7; }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
-
-// Issue this wave's share of the DMA for a [BC][D] tile starting at key k0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int k0, int Skv,
-                                         int wave, int lane) {
-  constexpr int CPR = FwdTile<D>::CPR;
-#pragma unroll
-  for (int j = 0; j < FwdTile<D>::DMA_PER_WAVE; ++j) {
-    const int blk = j * 4 + wave;
-    const int pos = blk * 64 + lane;             // physical chunk index in the tile
-    const int r = pos / CPR;
-    const int pc = pos % CPR;
-    const int lc = pc ^ (IS_V ? v_swz(r) : k_swz(r));
-    const int key = min(k0 + r, Skv - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * D + lc * 8),
-                                     (__attribute__((address_space(3))) void*)(dst + blk * 512),
-                                     16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
@@ -214,8 +183,8 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   // Start the first tile's transfer before anything else.
-  dma_tile<D, false>(Kh, sK[0], 0, Skv, wave, lane);
-  dma_tile<D, true>(Vh, sV[0], 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Kh, sK[0], 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Vh, sV[0], 0, Skv, wave, lane);
 
   // A negative scale is applied as |scale| on -Q (bf16 negation is exact),
   // so the maximum can be taken on raw scores and scaled afterwards.
@@ -238,21 +207,10 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   // Last key any row of this wave may see (tiles beyond it are skipped).
   const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
 
-  // Per-lane LDS offsets (elements).  K row reads: row kb*32 + swap23(n),
-  // logical chunk 2c + g, physical chunk (2c + g) ^ (n & 7).
-  const int k_row = swap23(n) * D;
-  int k_off[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) k_off[c] = k_row + 8 * ((2 * c + g) ^ (n & 7));
-  // V transpose reads: row r0 + (lane>>2)&3 with r0 = 32kb + 16c + 8g (+4),
-  // logical chunk 4db + 2((lane>>4)&1) + ((lane>>1)&1), element (lane&1)*4,
-  // physical chunk = logical ^ 2((lane>>2)&3).
-  const int vr = (lane >> 2) & 3;
-  const int v_lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-  int v_off[2];
-#pragma unroll
-  for (int dbp = 0; dbp < 2; ++dbp)
-    v_off[dbp] = (8 * g + vr) * D + 8 * ((4 * dbp + v_lc) ^ (2 * vr)) + 4 * (lane & 1);
+  // Per-lane LDS offsets (elements) into the swizzled tiles.
+  int k_off[4], v_off[2];
+  row_read_offsets<D>(n, g, k_off);
+  tr_read_offsets<D>(lane, v_off);
 
   float m_ref = kNegInf, lpart = 0.f;
 
@@ -323,8 +281,8 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     wait_vmcnt0();      // this wave's part of tile tt has landed in LDS
     __syncthreads();    // ... and every wave's; tile tt-1's buffer is free
     if (tt + 1 < n_tiles) {
-      dma_tile<D, false>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
-      dma_tile<D, true>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
     }
     if (k0 <= wave_kv_last) {
       const bool need_mask = (k0 + BC > Skv) || (CAUSAL && k0 + BC - 1 > wave_row0 + off);

@@ -45,7 +45,7 @@ struct BwdArgs {
   void* dv;
   int B, Hq, Hkv, Sq, Skv, d, causal;
   float scale;
-  float* ws;  // [B, Hq, Sq] D = rowsum(dO * O)
+  float* ws;  // [B, Hq, Sq] D = rowsum(dO * O), then [B, Hq, Sq] -LSE * log2(e)
   hipStream_t stream;
 };
 

@@ -58,7 +58,7 @@ def test_workspace_sizes():
     assert aos.attn_decode_workspace_bytes(8, 32, 128, 16) == 16 * 8 * 32 * 130 * 4
     assert aos.attn_decode_workspace_bytes(1, 1, 64, 1) == 512      # 66*4 rounded to 256
     assert aos.attn_decode_workspace_bytes(0, 1, 64, 1) == 0
-    assert aos.attn_bwd_workspace_bytes(4, 16, 2048, 128) == 4 * 16 * 2048 * 4
+    assert aos.attn_bwd_workspace_bytes(4, 16, 2048, 128) == 2 * 4 * 16 * 2048 * 4
     assert aos.attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
     assert aos.attn_bwd_workspace_bytes(1, -1, 1, 64) == 0
 
