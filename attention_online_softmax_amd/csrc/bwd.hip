@@ -91,12 +91,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int QB = BwdTile<D>::QB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][QB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG[2][QB * D];
-  __shared__ __attribute__((aligned(16))) float sDn[2][2 * QB];   // D then nl
+  // Double buffers as separate variables (see the forward kernel): the DMA
+  // into one buffer is then known not to alias the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QB * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QB * D];
+  __shared__ __attribute__((aligned(16))) float sDn0[2 * QB];   // D then nl
+  __shared__ __attribute__((aligned(16))) float sDn1[2 * QB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int bhk = blockIdx.x % BHk;
   const int ktile = blockIdx.x / BHk;
@@ -118,22 +123,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int n_qt = (Sq - q_start + QB - 1) / QB;  // query tiles per head
   const int n_it = G * n_qt;
 
-  auto issue = [&](int it, int buf) {
+  auto issue = [&](int it, uint16_t* dQt, uint16_t* dGt, float* dDn) {
     const int hh = it / n_qt;
     const int q0 = q_start + (it % n_qt) * QB;
     const int64_t bh = (int64_t)b * Hq + hk * G + hh;
-    dma_tile<D, QB, 4>(Q + bh * Sq * D, sQ[buf], q0, Sq, wave, lane);
-    dma_tile<D, QB, 4>(dO + bh * Sq * D, sG[buf], q0, Sq, wave, lane);
+    dma_tile<D, QB, 4>(Q + bh * Sq * D, dQt, q0, Sq, wave, lane);
+    dma_tile<D, QB, 4>(dO + bh * Sq * D, dGt, q0, Sq, wave, lane);
     if (wave < 2) {
       // wave 0: D of rows q0 .. q0+63, wave 1: nl of those rows, one float
       // per lane (rows past Sq repeat row Sq-1; they are masked).
       const float* src = (wave == 0 ? Dd : NL) + bh * Sq + min(q0 + lane, Sq - 1);
       __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)&sDn[buf][wave * QB],
+                                       (__attribute__((address_space(3))) void*)&dDn[wave * QB],
                                        4, 0, 0);
     }
   };
-  issue(0, 0);
+  issue(0, sQ0, sG0, sDn0);
 
   u32x4 kreg[NDC], vreg[NDC];
   const int krow = min(key, Skv - 1);
@@ -152,15 +157,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
-#pragma clang loop unroll(disable)
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
+  auto step = [&](const uint16_t* cQ, const uint16_t* cG, const float* cDn, uint16_t* nQ,
+                  uint16_t* nG, float* nDn, int it) {
     const int q0 = q_start + (it % n_qt) * QB;
     wait_vmcnt0();
     __syncthreads();
-    if (it + 1 < n_it) issue(it + 1, buf ^ 1);
-    const uint16_t* cQ = sQ[buf];
-    const uint16_t* cG = sG[buf];
+    if (it + 1 < n_it) issue(it + 1, nQ, nG, nDn);
 #pragma unroll
     for (int sb = 0; sb < QB / 32; ++sb) {
       const int qs = q0 + sb * 32;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dp = mfma32(*(const u32x4*)(gb + o), vreg[c], dp);
       }
       // Element i is query qs + 16*(i/8) + 8g + i%8 against key `key`.
-      const float* dn = &sDn[buf][sb * 32];
+      const float* dn = cDn + sb * 32;
       u32x4 pb[2], dsb[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -221,6 +223,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           dkt[db] = mfma32(tr_col8(qb + o, D), dsb[c], dkt[db]);
         }
     }
+  };
+#pragma clang loop unroll(disable)
+  for (int it = 0; it < n_it; it += 2) {
+    step(sQ0, sG0, sDn0, sQ1, sG1, sDn1, it);
+    if (it + 1 < n_it) step(sQ1, sG1, sDn1, sQ0, sG0, sDn0, it + 1);
   }
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
@@ -244,11 +251,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x % BH;
   const int t = blockIdx.x / BH;
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  dma_tile<D, BC, 4>(Kh, sK[0], 0, Skv, wave, lane);
-  dma_tile<D, BC, 4>(Vh, sV[0], 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Kh, sK0, 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Vh, sV0, 0, Skv, wave, lane);
 
   const int qrow = min(row, Sq - 1);
   const uint16_t* Qr = Q + ((int64_t)bh * Sq + qrow) * D;
@@ -292,18 +301,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
-#pragma clang loop unroll(disable)
-  for (int tt = 0; tt < n_tiles; ++tt) {
+  auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV, int tt) {
     const int k0 = tt * BC;
-    const int buf = tt & 1;
     wait_vmcnt0();
     __syncthreads();
     if (tt + 1 < n_tiles) {
-      dma_tile<D, BC, 4>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
-      dma_tile<D, BC, 4>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Kh, nK, k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Vh, nV, k0 + BC, Skv, wave, lane);
     }
-    const uint16_t* cK = sK[buf];
-    const uint16_t* cV = sV[buf];
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
       const int ks = k0 + kb * 32;
@@ -346,6 +351,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           dqt[db] = mfma32(tr_col8(kbp + o, D), dsb[c], dqt[db]);
         }
     }
+  };
+#pragma clang loop unroll(disable)
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    step(sK0, sV0, sK1, sV1, tt);
+    if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
   }
   if (!valid) return;
   store_transposed<NDB>(dQ + ((int64_t)bh * Sq + row) * D, dqt, g, scale);

@@ -57,6 +57,12 @@ __device__ __forceinline__ int swap23(int r) {
   return (r & ~0xc) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value, so that addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Lane exchange with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -126,16 +132,32 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
   constexpr int CPR = D / 8;
   constexpr int BLOCKS = ROWS * D / 512;
   static_assert(BLOCKS % NWAVES == 0, "tile must split evenly over the waves");
+  if (r0 + ROWS <= rlimit) {
+    // Full tile: a uniform base plus per-lane offsets that do not depend on
+    // the tile (addressing with a scalar base and a 32-bit vector offset).
+    const uint16_t* base = src + (int64_t)r0 * D;
 #pragma unroll
-  for (int j = 0; j < BLOCKS / NWAVES; ++j) {
-    const int blk = j * NWAVES + wave;
-    const int pos = blk * 64 + lane;
-    const int r = pos / CPR;
-    const int lc = (pos % CPR) ^ tile_swz(r);
-    const int row = min(r0 + r, rlimit - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * D + lc * 8),
-                                     (__attribute__((address_space(3))) void*)(dst + blk * 512),
-                                     16, 0, 0);
+    for (int j = 0; j < BLOCKS / NWAVES; ++j) {
+      const int blk = j * NWAVES + wave;
+      const int pos = blk * 64 + lane;
+      const int r = pos / CPR;
+      const int lc = (pos % CPR) ^ tile_swz(r);
+      __builtin_amdgcn_global_load_lds((const void*)(base + (r * D + lc * 8)),
+                                       (__attribute__((address_space(3))) void*)(dst + blk * 512),
+                                       16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < BLOCKS / NWAVES; ++j) {
+      const int blk = j * NWAVES + wave;
+      const int pos = blk * 64 + lane;
+      const int r = pos / CPR;
+      const int lc = (pos % CPR) ^ tile_swz(r);
+      const int row = min(r0 + r, rlimit - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * D + lc * 8),
+                                       (__attribute__((address_space(3))) void*)(dst + blk * 512),
+                                       16, 0, 0);
+    }
   }
 }
 

@@ -6,7 +6,8 @@
 // a monoid; "Compilers and Kernels", FlashAttention section, the recurrence's
 // state and O_i = o_T / l_T).  Scoring one token is a matrix-vector product,
 // so the split kernel is bound by streaming K and V from HBM: it reads each
-// key/value row once for all query heads that share it.
+// key/value row once for all query heads that share it, and issues all of a
+// sub-chunk's K and V loads before using any of them.
 #include "common.h"
 #include "launch.h"
 
@@ -21,9 +22,7 @@ struct Elem<float> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
   }
-  __device__ static void store(float* p, const float* f) {
-    *(f32x4*)p = f32x4{f[0], f[1], f[2], f[3]};
-  }
+  __device__ static void store2(float* p, float a, float b) { *(f32x2*)p = f32x2{a, b}; }
 };
 template <>
 struct Elem<uint16_t> {
@@ -35,208 +34,637 @@ struct Elem<uint16_t> {
       f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
     }
   }
-  __device__ static void store(uint16_t* p, const float* f) {
-    *(u32x4*)p = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
-  }
+  __device__ static void store2(uint16_t* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
 };
+
+// DPP lane permutations within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;      // row_ror:8 (lane i of a row reads lane (i + 8) % 16)
+
+// Sum (or max) over each aligned group of N consecutive lanes; every lane of
+// the group receives the result.  Steps: lane ^ 1, lane ^ 2 (quad perms),
+// mirror within 8 and within 16 (each pairs lanes whose partial results
+// cover disjoint halves), then lane ^ 16 (permlane16 swap: with both
+// operands x, the two results are x and x of lane ^ 16) and lane ^ 32.
+template <int N, bool MAX>
+__device__ __forceinline__ float group_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (N >= 2) x = op(x, dpp_mov<kQuadXor1>(x));
+  if constexpr (N >= 4) x = op(x, dpp_mov<kQuadXor2>(x));
+  if constexpr (N >= 8) x = op(x, dpp_mov<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = op(x, dpp_mov<kRowMirror>(x));
+  if constexpr (N >= 32) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (N >= 64) x = MAX ? halfwave_max(x) : halfwave_sum(x);
+  return x;
+}
 
 constexpr int kDecodeThreads = 256;
 
-// Grid: (n_splits, Hkv * n_hchunks, B).  Each workgroup owns one key chunk of
-// one key/value head and up to GC of its query heads.
-//   LPR lanes read one key row (16 bytes each), KPP rows are read per pass.
+// Persistent split kernel.  A work item is one key chunk (split) of one
+// key/value head for up to GC of its query heads.  Each workgroup walks the
+// items blockIdx.x, blockIdx.x + gridDim.x, ...; every item is cut into
+// stages of SK keys (64 KB of K and V), and the stages of all its items form
+// one stream: stage j+1 moves HBM -> LDS (global_load_lds) while stage j is
+// scored and accumulated from LDS.  Within an item the per-head state
+// (m, l, acc) is merged across stages by the online rescale; at the item's
+// end the partial accumulators of the key rows are reduced (lane swaps, then
+// LDS across waves) and the item's state is written to the workspace.
+template <typename T, int D>
+struct DecodeCfg {
+  static constexpr int E = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  static constexpr int CPR = D / E;                   // chunks per key row
+  static constexpr int LPR = CPR;                     // lanes per key row
+  static constexpr int KPP = kDecodeThreads / LPR;    // key rows per pass
+  static constexpr int SK = 32768 / (D * (int)sizeof(T));  // keys per stage
+  static constexpr int NP = SK / KPP;                 // passes per stage
+  static constexpr int STAGE = SK * D;                // elements per tensor per stage
+  static constexpr int BLOCKS = STAGE * (int)sizeof(T) / 1024;  // 1 KB DMA blocks per tensor
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void decode_dma(const T* src, T* dst, int L, int wave, int lane) {
+  using C = DecodeCfg<T, D>;
+  static_assert(C::BLOCKS % 4 == 0, "stage must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < C::BLOCKS / 4; ++j) {
+    const int blk = j * 4 + wave;
+    const int pos = blk * 64 + lane;                  // chunk index within the stage
+    const int r = min(pos / C::CPR, L - 1);           // rows past the chunk end repeat
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)r * D + (pos % C::CPR) * C::E),
+                                     (__attribute__((address_space(3))) void*)(dst + blk * 1024 / (int)sizeof(T)),
+                                     16, 0, 0);
+  }
+}
+
 template <typename T, int D, int GC>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ ws, int B, int Hq, int Hkv, int Skv, int chunk, int n_splits,
     int n_hchunks, float scale_log2) {
-  constexpr int E = Elem<T>::PER16;
-  constexpr int LPR = D / E;
-  constexpr int KPP = kDecodeThreads / LPR;
-  constexpr int MAXCHUNK = 1024;  // keys per workgroup held in LDS (host-checked)
-  __shared__ float sP[GC][MAXCHUNK];
-  __shared__ float sRed[KPP][D];
-  __shared__ float sStat[GC][2];
+  using C = DecodeCfg<T, D>;
+  constexpr int E = C::E, LPR = C::LPR, KPP = C::KPP, SK = C::SK, NP = C::NP;
+  constexpr int NW = kDecodeThreads / 64;
+  constexpr int RPW = 64 / LPR;  // key rows per wave
+  __shared__ __attribute__((aligned(1024))) T sK[2][C::STAGE];
+  __shared__ __attribute__((aligned(1024))) T sV[2][C::STAGE];
+  __shared__ float sMax[NW][GC];
+  __shared__ float sRed[NW][GC][D + 1];
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y / n_hchunks;
-  const int hc = blockIdx.y % n_hchunks;
-  const int b = blockIdx.z;
+  const int lane = tid & 63, wave = wave_id();
+  const int sub = tid % LPR;   // chunk (column slice) of this lane
+  const int kr = tid / LPR;    // key row within a pass
   const int G = Hq / Hkv;
-  const int h0 = hk * G + hc * GC;         // first query head of this workgroup
-  const int nh = min(GC, G - hc * GC);     // query heads handled here
-  const int k_begin = min(split * chunk, Skv);
-  const int k_end = min(k_begin + chunk, Skv);
-  const int L = k_end - k_begin;
   const int64_t BHq = (int64_t)B * Hq;
-
+  const int n_items = n_splits * Hkv * n_hchunks * B;
   float* ws_m = ws;
   float* ws_l = ws + (int64_t)n_splits * BHq;
   float* ws_acc = ws + 2 * (int64_t)n_splits * BHq;
 
-  if (L <= 0) {  // empty chunk: the identity state
+  struct Item {
+    int split, hk, hc, b, k_begin, L, n_st;
+  };
+  auto item_of = [&](int it) {
+    Item x;
+    x.split = it % n_splits;
+    int r = it / n_splits;
+    x.hc = r % n_hchunks;
+    r /= n_hchunks;
+    x.hk = r % Hkv;
+    x.b = r / Hkv;
+    x.k_begin = min(x.split * chunk, Skv);
+    x.L = min(x.k_begin + chunk, Skv) - x.k_begin;
+    x.n_st = (x.L + SK - 1) / SK;
+    return x;
+  };
+  // Issue the DMA of stage `st` of item `x` into buffer `buf`.
+  auto issue = [&](const Item& x, int st, int buf) {
+    const int64_t base = ((int64_t)(x.b * Hkv + x.hk) * Skv + x.k_begin + st * SK) * D;
+    const int Ls = min(SK, x.L - st * SK);
+    decode_dma<T, D>(K + base, sK[buf], Ls, wave, lane);
+    decode_dma<T, D>(V + base, sV[buf], Ls, wave, lane);
+  };
+
+  int it = blockIdx.x;
+  // Skip leading empty items (identity states are written without a stage).
+  auto write_identity = [&](const Item& x) {
+    const int h0 = x.hk * G + x.hc * GC;
+    const int nh = min(GC, G - x.hc * GC);
     for (int i = tid; i < nh * D; i += kDecodeThreads) {
       const int hh = i / D, dd = i % D;
-      const int64_t idx = (int64_t)split * BHq + (int64_t)b * Hq + h0 + hh;
+      const int64_t idx = (int64_t)x.split * BHq + (int64_t)x.b * Hq + h0 + hh;
       ws_acc[idx * D + dd] = 0.f;
       if (dd == 0) {
         ws_m[idx] = kNegInf;
         ws_l[idx] = 0.f;
       }
     }
-    return;
+  };
+  while (it < n_items && item_of(it).L <= 0) {
+    write_identity(item_of(it));
+    it += gridDim.x;
   }
+  if (it >= n_items) return;
 
-  const int sub = tid % LPR;   // which 16-byte column slice
-  const int kr = tid / LPR;    // which key row of a pass
-  const T* Kh = K + ((int64_t)(b * Hkv + hk) * Skv + k_begin) * D + sub * E;
-  const T* Vh = V + ((int64_t)(b * Hkv + hk) * Skv + k_begin) * D + sub * E;
+  Item cur = item_of(it);
+  int st = 0, buf = 0;
+  issue(cur, 0, 0);
 
-  // This lane's slice of each query head, pre-scaled into the log2 domain.
-  float q[GC][E];
-#pragma unroll
-  for (int hh = 0; hh < GC; ++hh) {
-    if (hh < nh) {
-      const T* qp = Q + ((int64_t)b * Hq + h0 + hh) * D + sub * E;
-      float f[E];
-      Elem<T>::unpack(*(const u32x4*)qp, f);
-#pragma unroll
-      for (int e = 0; e < E; ++e) q[hh][e] = f[e] * scale_log2;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) q[hh][e] = 0.f;
+  float q[GC][E], m[GC], lsum[GC], acc[GC][E];
+  bool fresh = true;  // first stage of the current item
+
+  while (true) {
+    // Next stage in the stream (same item or the next non-empty one).
+    Item nxt = cur;
+    int nst = st + 1;
+    int nit = it;
+    if (nst >= cur.n_st) {
+      nst = 0;
+      nit = it + gridDim.x;
+      while (nit < n_items && item_of(nit).L <= 0) {
+        write_identity(item_of(nit));
+        nit += gridDim.x;
+      }
+      if (nit < n_items) nxt = item_of(nit);
     }
-  }
+    const bool has_next = nit < n_items;
 
-  // Phase 1: scores of every key in the chunk for every query head.
-  constexpr int U = 4;  // passes in flight
-  for (int p0 = 0; p0 < L; p0 += KPP * U) {
-    u32x4 kx[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = p0 + u * KPP + kr;
-      kx[u] = (r < L) ? *(const u32x4*)(Kh + (int64_t)r * D) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[E];
-      Elem<T>::unpack(kx[u], f);
-      const int r = p0 + u * KPP + kr;
+    const int h0 = cur.hk * G + cur.hc * GC;
+    const int nh = min(GC, G - cur.hc * GC);
+    if (fresh) {
 #pragma unroll
       for (int hh = 0; hh < GC; ++hh) {
-        float acc = 0.f;
+        const int hq = h0 + min(hh, nh - 1);
+        float f[E];
+        Elem<T>::unpack(*(const u32x4*)(Q + ((int64_t)cur.b * Hq + hq) * D + sub * E), f);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc = fmaf(q[hh][e], f[e], acc);
+        for (int e = 0; e < E; ++e) q[hh][e] = f[e] * scale_log2;
+        m[hh] = kNegInf;
+        lsum[hh] = 0.f;
 #pragma unroll
-        for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
-        if (sub == 0 && r < L && hh < nh) sP[hh][r] = acc;
+        for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
+      }
+      fresh = false;
+    }
+
+    wait_vmcnt0();     // this wave's part of the current stage is in LDS
+    __syncthreads();   // every wave's part; the other buffer is free
+    if (has_next) issue(nxt, nst, buf ^ 1);
+
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
+    const int Ls = min(SK, cur.L - st * SK);
+    float s[GC][NP], tmax[GC];
+#pragma unroll
+    for (int hh = 0; hh < GC; ++hh) tmax[hh] = kNegInf;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = p * KPP + kr;
+      float f[E];
+      Elem<T>::unpack(*(const u32x4*)(cK + r * D + sub * E), f);
+#pragma unroll
+      for (int hh = 0; hh < GC; ++hh) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaf(q[hh][e], f[e], a);
+        a = group_reduce<LPR, false>(a);
+        s[hh][p] = (r < Ls) ? a : kNegInf;
+        tmax[hh] = fmaxf(tmax[hh], s[hh][p]);
       }
     }
-  }
-  __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < GC; ++hh) {
+      float x = tmax[hh];
+      if constexpr (LPR < 16) x = group_reduce<16, true>(x);
+      if constexpr (LPR < 32) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      if constexpr (LPR < 64) x = halfwave_max(x);
+      if (lane == 0) sMax[wave][hh] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < GC; ++hh) {
+      float mx = sMax[0][hh];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sMax[w][hh]);
+      const float mnew = fmaxf(m[hh], mx);           // finite: the stage is non-empty
+      const float alpha = fast_exp2(m[hh] - mnew);   // 0 on the item's first stage
+      m[hh] = mnew;
+      lsum[hh] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[hh][e] *= alpha;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = p * KPP + kr;
+      float f[E];
+      Elem<T>::unpack(*(const u32x4*)(cV + r * D + sub * E), f);
+#pragma unroll
+      for (int hh = 0; hh < GC; ++hh) {
+        const float pw = fast_exp2(s[hh][p] - m[hh]);
+        lsum[hh] += pw;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pw, f[e], acc[hh][e]);
+      }
+    }
 
-  // Phase 2: per query head, chunk maximum m, p = exp2(s - m), l = sum p.
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int hh = wave; hh < nh; hh += kDecodeThreads / 64) {
-    float mx = kNegInf;
-    for (int r = lane; r < L; r += 64) mx = fmaxf(mx, sP[hh][r]);
+    if (st + 1 >= cur.n_st) {
+      // Item done: reduce over key rows (rows of a wave by lane swaps, the
+      // waves through LDS) and write its state.
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w));
-    float sum = 0.f;
-    for (int r = lane; r < L; r += 64) {
-      const float p = fast_exp2(sP[hh][r] - mx);
-      sP[hh][r] = p;
-      sum += p;
-    }
+      for (int hh = 0; hh < GC; ++hh) {
+        float l = lsum[hh];  // identical across the lanes of a row group
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) sum += __shfl_xor(sum, w);
-    if (lane == 0) {
-      sStat[hh][0] = mx;
-      sStat[hh][1] = sum;
-    }
-  }
-  __syncthreads();
-
-  // Phase 3: acc[h][:] = sum_r p[h][r] V[r][:], this lane's column slice and
-  // every KPP-th key, then reduced over the KPP key groups through LDS.
-  float acc[GC][E];
+        for (int e = 0; e < E; ++e) {
+          float x = acc[hh][e];
+          if constexpr (RPW >= 2) {
+            if constexpr (LPR == 32) {
+              auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+              x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            } else if constexpr (LPR == 16) {
+              auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+              x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+              x = halfwave_sum(x);
+            } else {  // LPR == 8: lanes i and i ^ 8 hold the same columns
+              x += dpp_mov<kRowRor8>(x);
+              auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+              x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+              x = halfwave_sum(x);
+            }
+          }
+          if (lane < LPR) sRed[wave][hh][sub * E + e] = x;
+        }
+        if constexpr (RPW >= 2) {
+          if constexpr (LPR == 32) {
+            l = halfwave_sum(l);
+          } else if constexpr (LPR == 16) {
+            auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+            l = halfwave_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+          } else {
+            l += dpp_mov<kRowRor8>(l);
+            auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+            l = halfwave_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+          }
+        }
+        if (lane == 0) sRed[wave][hh][D] = l;
+      }
+      __syncthreads();
+      for (int i = tid; i < nh * (D + 1); i += kDecodeThreads) {
+        const int hh = i / (D + 1), dd = i % (D + 1);
+        float t = 0.f;
 #pragma unroll
-  for (int hh = 0; hh < GC; ++hh)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
-  for (int p0 = 0; p0 < L; p0 += KPP * U) {
-    u32x4 vx[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = p0 + u * KPP + kr;
-      vx[u] = (r < L) ? *(const u32x4*)(Vh + (int64_t)r * D) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = p0 + u * KPP + kr;
-      if (r < L) {
-        float f[E];
-        Elem<T>::unpack(vx[u], f);
-#pragma unroll
-        for (int hh = 0; hh < GC; ++hh) {
-          const float p = (hh < nh) ? sP[hh][r] : 0.f;
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(p, f[e], acc[hh][e]);
+        for (int w = 0; w < NW; ++w) t += sRed[w][hh][dd];
+        const int64_t idx = (int64_t)cur.split * BHq + (int64_t)cur.b * Hq + h0 + hh;
+        if (dd < D) {
+          ws_acc[idx * D + dd] = t;
+        } else {
+          ws_l[idx] = t;
+          ws_m[idx] = m[hh];
         }
       }
+      fresh = true;
     }
-  }
-  for (int hh = 0; hh < nh; ++hh) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) sRed[kr][sub * E + e] = acc[hh][e];
-    __syncthreads();
-    const int64_t idx = (int64_t)split * BHq + (int64_t)b * Hq + h0 + hh;
-    for (int dd = tid; dd < D; dd += kDecodeThreads) {
-      float s = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < KPP; ++r) s += sRed[r][dd];
-      ws_acc[idx * D + dd] = s;
-    }
-    if (tid == 0) {
-      ws_m[idx] = sStat[hh][0];
-      ws_l[idx] = sStat[hh][1];
-    }
-    __syncthreads();
+    if (!has_next) break;
+    // sMax / sRed are rewritten by the next stage only after its barrier.
+    cur = nxt;
+    st = nst;
+    it = nit;
+    buf ^= 1;
   }
 }
 
-// Grid: B * Hq workgroups of D threads.  Folds the n_splits states of one
-// query with the monoid merge: every state is rescaled by exp2(m_s - M),
-// M = max_s m_s (identity states, m_s = -inf, get weight 0), then O = acc / l
-// and LSE = (M + log2 l) ln 2.
+// ---------------------------------------------------------------------------
+// bf16 split kernel on the matrix cores.  A work unit is one key chunk
+// (split) of one key/value head for up to 8 of its query heads.  The query
+// heads take the place of the query rows of the forward kernel (32 MFMA
+// columns; the ones past the group's heads are fed zeros): per tile of 32
+// keys, S^T = K Q^T (lane = head, 16 scores per lane), the running
+// (m, l, o) per head, and O^T += V^T P^T with V^T from transpose reads.
+//
+// Work is assigned per wave: wave w of the grid takes units w, w + W, ...
+// (W = waves in the grid).  Each wave streams its units' tiles through its
+// own pair of LDS buffers with global_load_lds, tile t+1 in flight while
+// tile t is used (across unit boundaries too), and writes each unit's state
+// straight from registers.  No barriers: the waves of a workgroup share only
+// the LDS allocation.
+// ---------------------------------------------------------------------------
+constexpr float kDecodeLazy = 8.f;  // lazy rescale threshold (log2 units), as in the forward
+constexpr int kDecodeHC = 8;        // query heads per work unit on the matrix cores
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ ws, int B, int Hq, int Hkv, int Skv,
+    int chunk, int n_splits, int n_hchunks, float scale_log2) {
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TK = 32;  // keys per tile
+  constexpr int HC = kDecodeHC;
+  // Each wave's two tile buffers live in separate variables so that the
+  // compiler sees the DMA into one cannot alias the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t sKa[4][TK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sKb[4][TK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sVa[4][TK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sVb[4][TK * D];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 31, g = lane >> 5;
+  const int G = Hq / Hkv;
+  const int64_t BHq = (int64_t)B * Hq;
+  const int n_units = n_splits * Hkv * n_hchunks * B;
+  const int W = gridDim.x * 4;
+  float* ws_m = ws;
+  float* ws_l = ws + (int64_t)n_splits * BHq;
+  float* ws_acc = ws + 2 * (int64_t)n_splits * BHq;
+
+  struct Unit {
+    int split, hk, hc, b, k0, L;  // keys [k0, k0 + L) of key/value head (b, hk)
+    int rot;                      // tile t of the unit is its tile (t + rot) % n_tiles
+  };
+  auto unit_of = [&](int u) {
+    Unit x;
+    x.split = u % n_splits;
+    int r = u / n_splits;
+    x.hc = r % n_hchunks;
+    r /= n_hchunks;
+    x.hk = r % Hkv;
+    x.b = r / Hkv;
+    x.k0 = min(x.split * chunk, Skv);
+    x.L = min(x.k0 + chunk, Skv) - x.k0;
+    // Concurrent waves start at different tiles of their chunks, so that they
+    // do not all read the same offsets of equally strided chunks at once.
+    const int nt = (x.L + TK - 1) / TK;
+    x.rot = nt > 0 ? (u / n_splits + x.split) % nt : 0;
+    return x;
+  };
+  auto n_tiles = [&](const Unit& x) { return (x.L + TK - 1) / TK; };
+  auto tile_of = [&](const Unit& x, int t) {
+    const int nt = n_tiles(x);
+    const int tt = t + x.rot;
+    return tt >= nt ? tt - nt : tt;
+  };
+  auto issue = [&](const Unit& x, int t, uint16_t* dK, uint16_t* dV) {
+    const int64_t base = (int64_t)(x.b * Hkv + x.hk) * Skv * D;
+    const int r0 = x.k0 + tile_of(x, t) * TK;
+    dma_tile<D, TK, 1>(K + base, dK, r0, x.k0 + x.L, 0, lane);
+    dma_tile<D, TK, 1>(V + base, dV, r0, x.k0 + x.L, 0, lane);
+  };
+  // Raw query rows of the unit's heads (lanes past the group's heads load a
+  // valid row and are zeroed by q_keep when the rows are adopted, so that
+  // no instruction depends on the load before the unit starts).
+  auto load_q = [&](const Unit& x, u32x4* qr) {
+    const int nh = min(HC, G - x.hc * HC);
+    const int hq = x.hk * G + x.hc * HC + min(n, nh - 1);
+    const uint16_t* qp = Q + ((int64_t)x.b * Hq + hq) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) qr[c] = *(const u32x4*)(qp + c * 16);
+  };
+  auto q_keep = [&](const Unit& x) {
+    return (n < min(HC, G - x.hc * HC)) ? 0xffffffffu : 0u;
+  };
+  auto write_state = [&](const Unit& x, float m, float lpart, const f32x16* oacc) {
+    const int nh = min(HC, G - x.hc * HC);
+    const float l = halfwave_sum(lpart);
+    if (n < nh) {
+      const int64_t idx =
+          (int64_t)x.split * BHq + (int64_t)x.b * Hq + x.hk * G + x.hc * HC + n;
+      float* dst = ws_acc + idx * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *(f32x4*)(dst + db * 32 + 8 * i4 + 4 * g) =
+              f32x4{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3]};
+      if (g == 0) {
+        ws_m[idx] = m;   // log2 domain, like every partial
+        ws_l[idx] = l;
+      }
+    }
+  };
+
+  int u = blockIdx.x * 4 + wave;
+  // Units with no keys get the identity state and no tiles.
+  while (u < n_units && unit_of(u).L <= 0) {
+    f32x16 z[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[db][i] = 0.f;
+    write_state(unit_of(u), kNegInf, 0.f, z);
+    u += W;
+  }
+  if (u >= n_units) return;
+
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c2 = fabsf(scale_log2);
+  int r_off[4], t_off[2];
+  row_read_offsets<D>(n, g, r_off);
+  tr_read_offsets<D>(lane, t_off);
+
+  Unit cur = unit_of(u);
+  u32x4 qreg[NDC], qnext[NDC];
+  load_q(cur, qreg);
+  {
+    const uint32_t keep = q_keep(cur);
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) qreg[c] &= keep;
+  }
+  issue(cur, 0, sKa[wave], sVa[wave]);
+  int t = 0;
+  bool new_q = false;
+  float m_ref = kNegInf, lpart = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+
+  // One tile of this wave's stream; returns false after the last tile.
+  auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) -> bool {
+    const int nt = n_tiles(cur);
+    Unit nxt = cur;
+    int tn = t + 1, un = u;
+    const bool unit_end = tn >= nt;
+    if (unit_end) {
+      tn = 0;
+      un = u + W;
+      while (un < n_units && unit_of(un).L <= 0) {
+        f32x16 z[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[db][i] = 0.f;
+        write_state(unit_of(un), kNegInf, 0.f, z);
+        un += W;
+      }
+      if (un < n_units) nxt = unit_of(un);
+    }
+    const bool more = un < n_units;
+
+    wait_vmcnt0();   // tile t (and every earlier load of this wave) has landed
+    if (new_q) {
+      const uint32_t keep = q_keep(cur);
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) qreg[c] = qnext[c] & keep;
+      new_q = false;
+    }
+    if (!unit_end || more) {
+      issue(nxt, tn, nK, nV);
+      if (unit_end) load_q(nxt, qnext);
+    }
+
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c)
+      s = mfma32(*(const u32x4*)(cK + r_off[c & 3] + 64 * (c >> 2)), qreg[c] ^ qsign, s);
+    const int kvalid = cur.L - tile_of(cur, t) * TK;  // keys of this tile that exist
+    float rmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = 16 * (i >> 3) + 8 * g + (i & 7);
+      s[i] = (kk < kvalid) ? s[i] : kNegInf;
+      rmax = fmaxf(rmax, s[i]);
+    }
+    const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
+    if (__any(mnew > m_ref + kDecodeLazy)) {
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_ref = mnew;
+    }
+    const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
+    u32x4 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(fmaf(s[8 * c + 2 * j], c2, -msub));
+        const float p1 = fast_exp2(fmaf(s[8 * c + 2 * j + 1], c2, -msub));
+        lpart += p0 + p1;
+        pb[c][j] = pack_bf16x2(p0, p1);
+      }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(tr_col8(cV + 16 * c * D + t_off[db & 1] + 64 * (db >> 1), D), pb[c],
+                          oacc[db]);
+
+    if (unit_end) {
+      write_state(cur, m_ref, lpart, oacc);
+      if (!more) return false;
+      m_ref = kNegInf;
+      lpart = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+      new_q = true;
+      cur = nxt;
+      u = un;
+    }
+    t = tn;
+    return true;
+  };
+  while (step(sKa[wave], sVa[wave], sKb[wave], sVb[wave]) &&
+         step(sKb[wave], sVb[wave], sKa[wave], sVa[wave])) {
+  }
+}
+
+// One wave per query (b, h): lanes hold the split states (m_s, l_s) in
+// parallel, the wave computes M = max_s m_s and the weights exp2(m_s - M)
+// (identity states, m_s = -inf, weigh 0), then every lane folds two output
+// columns over the splits: O = sum_s w_s acc_s / sum_s w_s l_s and
+// LSE = (M + log2 l) ln 2.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws,
-                                                           T* __restrict__ O,
-                                                           float* __restrict__ LSE, int BHq,
-                                                           int n_splits) {
-  const int bh = blockIdx.x;
-  const int dd = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ ws,
+                                                             T* __restrict__ O,
+                                                             float* __restrict__ LSE, int BHq,
+                                                             int n_splits) {
+  constexpr int CPL = D / 64;  // columns per lane (1, 2 or 4)
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BHq) return;
   const float* ws_m = ws;
   const float* ws_l = ws + (int64_t)n_splits * BHq;
   const float* ws_acc = ws + 2 * (int64_t)n_splits * BHq;
   float M = kNegInf;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_m[(int64_t)s * BHq + bh]);
-  float l = 0.f, a = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = ws_m[(int64_t)s * BHq + bh];
-    const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-    l = fmaf(w, ws_l[(int64_t)s * BHq + bh], l);
-    a = fmaf(w, ws_acc[((int64_t)s * BHq + bh) * D + dd], a);
+  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, ws_m[(int64_t)s * BHq + bh]);
+  M = group_reduce<64, true>(M);
+  float l = 0.f, a[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) a[c] = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < n_splits) {
+      const float ms = ws_m[(int64_t)s * BHq + bh];
+      w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+      l = fmaf(w, ws_l[(int64_t)s * BHq + bh], l);
+    }
+    const int ns = min(64, n_splits - s0);
+    // Groups of 16 splits: all loads of a group are issued before use.
+    for (int j0 = 0; j0 < ns; j0 += 16) {
+      float v[16][CPL];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int sj = s0 + min(j0 + j, ns - 1);
+        const float* src = ws_acc + ((int64_t)sj * BHq + bh) * D + lane * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[j][c] = src[c];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float wj = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j0 + j, 63)));
+        const float wjm = (j0 + j < ns) ? wj : 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) a[c] = fmaf(wjm, v[j][c], a[c]);
+      }
+    }
   }
-  const float r = a / l;
-  if constexpr (sizeof(T) == 4) {
-    O[(int64_t)bh * D + dd] = r;
+  l = group_reduce<64, false>(l);
+  const float inv = 1.f / l;
+  T* o = O + (int64_t)bh * D + lane * CPL;
+  if constexpr (CPL == 1) {
+    if constexpr (sizeof(T) == 4) {
+      o[0] = a[0] * inv;
+    } else {
+      o[0] = f32_to_bf16(a[0] * inv);
+    }
   } else {
-    O[(int64_t)bh * D + dd] = f32_to_bf16(r);
+#pragma unroll
+    for (int c = 0; c < CPL; c += 2) Elem<T>::store2(o + c, a[c] * inv, a[c + 1] * inv);
   }
-  if (LSE && dd == 0) LSE[bh] = (M + fast_log2(l)) * kLn2;
+  if (LSE && lane == 0) LSE[bh] = (M + fast_log2(l)) * kLn2;
+}
+
+// Compute units of the current device (one persistent split workgroup each).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
 }
 
 template <typename T, int D, int GC>
@@ -244,17 +672,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int G = a.Hq / a.Hkv;
   const int n_hchunks = (G + GC - 1) / GC;
   const int chunk = (a.Skv + a.n_splits - 1) / a.n_splits;
-  dim3 grid(a.n_splits, a.Hkv * n_hchunks, a.B);
+  const int n_items = a.n_splits * a.Hkv * n_hchunks * a.B;
+  const int grid = n_items < device_cus() ? n_items : device_cus();
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), grid, dim3(kDecodeThreads), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.ws, a.B, a.Hq, a.Hkv, a.Skv,
-                     chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3(grid), dim3(kDecodeThreads), 0,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.ws, a.B, a.Hq,
+                     a.Hkv, a.Skv, chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int BHq = a.B * a.Hq;
   timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, a.stream,
-                     (const float*)a.ws, (T*)a.o, a.lse, a.B * a.Hq, a.n_splits);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((BHq + 3) / 4), dim3(256), 0, a.stream,
+                     (const float*)a.ws, (T*)a.o, a.lse, BHq, a.n_splits);
   timing_mark(a.stream, 3);
   return hipGetLastError();
 }
@@ -264,12 +694,44 @@ static hipError_t dispatch_decode_g(const DecodeArgs& a) {
   const int G = a.Hq / a.Hkv;
   if (G == 1) return launch_decode_t<T, D, 1>(a);
   if (G == 2) return launch_decode_t<T, D, 2>(a);
-  if (G <= 4) return launch_decode_t<T, D, 4>(a);
-  return launch_decode_t<T, D, 8>(a);
+  if constexpr (D > 128) {
+    return launch_decode_t<T, D, 4>(a);  // 8 heads x 256 columns exceed the LDS budget
+  } else {
+    if (G <= 4) return launch_decode_t<T, D, 4>(a);
+    return launch_decode_t<T, D, 8>(a);
+  }
+}
+
+template <int D>
+static hipError_t launch_decode_mfma(const DecodeArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  const int n_hchunks = (G + kDecodeHC - 1) / kDecodeHC;
+  const int chunk = (a.Skv + a.n_splits - 1) / a.n_splits;
+  const int n_units = a.n_splits * a.Hkv * n_hchunks * a.B;
+  // One workgroup (four waves) per compute unit, each wave a stream of units.
+  const int wgs = (n_units + 3) / 4;
+  const int grid = wgs < device_cus() ? wgs : device_cus();
+  timing_mark(a.stream, 0);
+  hipLaunchKernelGGL((decode_split_mfma_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws, a.B,
+                     a.Hq, a.Hkv, a.Skv, chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
+  timing_mark(a.stream, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int BHq = a.B * a.Hq;
+  timing_mark(a.stream, 2);
+  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3((BHq + 3) / 4), dim3(256), 0,
+                     a.stream, (const float*)a.ws, (uint16_t*)a.o, a.lse, BHq, a.n_splits);
+  timing_mark(a.stream, 3);
+  return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t dispatch_decode_d(const DecodeArgs& a) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.d == 64) return launch_decode_mfma<64>(a);
+    if (a.d == 128) return launch_decode_mfma<128>(a);
+  }
   switch (a.d) {
     case 64: return dispatch_decode_g<T, 64>(a);
     case 128: return dispatch_decode_g<T, 128>(a);
@@ -277,9 +739,6 @@ static hipError_t dispatch_decode_d(const DecodeArgs& a) {
   }
   return hipErrorInvalidValue;
 }
-
-// Largest key chunk one split workgroup can hold (its LDS score buffer).
-int decode_max_chunk() { return 1024; }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   return a.dtype == 0 ? dispatch_decode_d<float>(a) : dispatch_decode_d<uint16_t>(a);

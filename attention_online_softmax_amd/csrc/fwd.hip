@@ -158,11 +158,16 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BC * D];
+  // Two buffers per tensor as separate variables: the compiler can then see
+  // that the DMA into one buffer does not alias the reads of the other and
+  // does not wait for the DMA before those reads.
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x % BH;
   const int t = blockIdx.x / BH;
@@ -183,8 +188,8 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   // Start the first tile's transfer before anything else.
-  dma_tile<D, BC, 4>(Kh, sK[0], 0, Skv, wave, lane);
-  dma_tile<D, BC, 4>(Vh, sV[0], 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Kh, sK0, 0, Skv, wave, lane);
+  dma_tile<D, BC, 4>(Vh, sV0, 0, Skv, wave, lane);
 
   // A negative scale is applied as |scale| on -Q (bf16 negation is exact),
   // so the maximum can be taken on raw scores and scaled afterwards.
@@ -274,20 +279,25 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
         }
   };
 
-#pragma clang loop unroll(disable)
-  for (int tt = 0; tt < n_tiles; ++tt) {
+  // One tile step: wait for tile tt, start tile tt+1 into the other buffer,
+  // then use tile tt.
+  auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV, int tt) {
     const int k0 = tt * BC;
-    const int buf = tt & 1;
     wait_vmcnt0();      // this wave's part of tile tt has landed in LDS
-    __syncthreads();    // ... and every wave's; tile tt-1's buffer is free
+    __syncthreads();    // ... and every wave's; the other buffer is free
     if (tt + 1 < n_tiles) {
-      dma_tile<D, BC, 4>(Kh, sK[buf ^ 1], k0 + BC, Skv, wave, lane);
-      dma_tile<D, BC, 4>(Vh, sV[buf ^ 1], k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Kh, nK, k0 + BC, Skv, wave, lane);
+      dma_tile<D, BC, 4>(Vh, nV, k0 + BC, Skv, wave, lane);
     }
     if (k0 <= wave_kv_last) {
       const bool need_mask = (k0 + BC > Skv) || (CAUSAL && k0 + BC - 1 > wave_row0 + off);
-      tile(sK[buf], sV[buf], k0, need_mask);
+      tile(cK, cV, k0, need_mask);
     }
+  };
+#pragma clang loop unroll(disable)
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    step(sK0, sV0, sK1, sV1, tt);
+    if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
   }
 
   const float l = halfwave_sum(lpart);
