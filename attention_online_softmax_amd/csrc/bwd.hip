@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkt[db][i] = dvt[db][i] = 0.f;
 
-  int r_off[4], t_off[2];
+  int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const uint16_t* gb = cG + sb * 32 * D;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        const int o = r_off[c & 3] + 64 * (c >> 2);
+        const int o = row_off<D>(r_off, c);
         s = mfma32(*(const u32x4*)(qb + o), kreg[c], s);
         dp = mfma32(*(const u32x4*)(gb + o), vreg[c], dp);
       }
@@ -218,9 +218,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int o = 16 * c * D + t_off[db & 1] + 64 * (db >> 1);
-          dvt[db] = mfma32(tr_col8(gb + o, D), pb[c], dvt[db]);
-          dkt[db] = mfma32(tr_col8(qb + o, D), dsb[c], dkt[db]);
+          dvt[db] = mfma32(tr_col8<D>(gb + 16 * c * D, t_off, db), pb[c], dvt[db]);
+          dkt[db] = mfma32(tr_col8<D>(qb + 16 * c * D, t_off, db), dsb[c], dkt[db]);
         }
     }
   };
@@ -297,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
   const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
-  int r_off[4], t_off[2];
+  int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       const uint16_t* vbp = cV + kb * 32 * D;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        const int o = r_off[c & 3] + 64 * (c >> 2);
+        const int o = row_off<D>(r_off, c);
         s = mfma32(*(const u32x4*)(kbp + o), qreg[c], s);
         dp = mfma32(*(const u32x4*)(vbp + o), greg[c], dp);
       }
@@ -347,8 +346,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int o = 16 * c * D + t_off[db & 1] + 64 * (db >> 1);
-          dqt[db] = mfma32(tr_col8(kbp + o, D), dsb[c], dqt[db]);
+          dqt[db] = mfma32(tr_col8<D>(kbp + 16 * c * D, t_off, db), dsb[c], dqt[db]);
         }
     }
   };

@@ -89,38 +89,56 @@ __device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Per-lane offset (in elements) for tr_col8 within a row-major LDS tile of
-// the given pitch.
-__device__ __forceinline__ int tr_lane_offset(int lane, int pitch) {
-  return ((lane >> 2) & 3) * pitch + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-}
-
-// k-operand of a 32x32x16 MFMA contracted over 8 consecutive ROWS of a
-// row-major LDS tile: lane l gets rows r0 .. r0+7 (r0 = base + 8*(l/32),
-// uniform per 16-lane group) of column c0 + l%32.  `p` = tile + r0*pitch +
-// c0 + tr_lane_offset(lane, pitch).
-__device__ __forceinline__ u32x4 tr_col8(const uint16_t* p, int pitch) {
-  const u32x2 a = lds_tr4(p);
-  const u32x2 b = lds_tr4(p + 4 * pitch);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 // ---------------------------------------------------------------------------
-// Swizzled [ROWS][D] bf16 tiles in LDS, filled by global_load_lds.
+// Swizzled [ROWS][D] bf16 tiles in LDS, filled by loads to LDS.
 //
-// Rows are dense (D * 2 bytes); within each aligned group of eight 16-byte
-// chunks, logical chunk c of row r is stored at chunk c ^ tile_swz(r) with
-// tile_swz(r) = 2 (r & 3) | ((r >> 3) & 1).  LDS has 32 banks of 4 bytes
-// (128 bytes per cycle), so:
-//  * a b128 row read where lanes 0..7 take rows swap23(0..7) =
-//    {0,1,2,3,8,9,10,11} (plus a multiple of 32) at one logical chunk hits 8
-//    distinct chunk positions of a 128-byte window;
-//  * a transpose read where 16 lanes take 4 consecutive rows (starting at a
-//    multiple of 4) x 32 bytes hits 4 distinct 32-byte windows.
+// Rows are dense (D * 2 bytes).  Logical 16-byte chunk k of row r is stored
+// at chunk k ^ tile_swz<D>(r); the XOR stays inside aligned groups of 16
+// chunks (8 for D = 64).  LDS has 64 banks of 4 bytes (256 bytes per cycle);
+// a b128 read is served 16 lanes per cycle and a b64 transpose read 32 lanes
+// per cycle.  The swizzle makes both access patterns of the kernels free of
+// bank conflicts:
+//  * b128 row reads: 16 lanes take the 16 rows of an aligned 16-row group at
+//    one logical chunk; tile_swz is a bijection of r & 15 (of bits 1..3 for
+//    D = 64, where bit 0 picks the half of the 256-byte bank window);
+//  * transpose reads: 32 lanes take 4 consecutive rows (from a multiple of 4)
+//    x 64 bytes; bits 3..2 of tile_swz (bit 2 with the row parity for D = 64)
+//    place those rows in the 4 distinct 64-byte quarters of the bank window.
+// Rows r and r + 4 (r & 4 == 0) differ only in the top bit of the swizzle, so
+// the second half of an 8-row transpose read reuses the offset of another
+// 32-column block (tr_col8).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int tile_swz(int r) { return (2 * (r & 3)) | ((r >> 3) & 1); }
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D >= 128)
+    return ((((r >> 2) ^ (r >> 1)) & 1) << 3) | ((r & 1) << 2) | (((r >> 3) & 1) << 1) |
+           ((r >> 1) & 1);
+  else
+    return ((((r >> 1) ^ (r >> 2)) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 1) & 1);
+}
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
+// Workgroup barrier for LDS tiles filled by loads to LDS, without the
+// release/acquire fences of __syncthreads (which wait for every load in
+// flight, including prefetches of later tiles).  Callers wait for their own
+// transfers of the tile (wait_vmcnt) before it; every LDS read issued before
+// it has been consumed by then.  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (they complete in issue order, so everything older than the newest N has
+// landed).  gfx9 encoding: vmcnt in bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
 
 // This wave's share of the transfer of rows r0 .. r0+ROWS-1 of a row-major
 // [*, D] bf16 matrix (rows at or beyond rlimit read row rlimit-1 instead)
@@ -141,7 +159,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
       const int blk = j * NWAVES + wave;
       const int pos = blk * 64 + lane;
       const int r = pos / CPR;
-      const int lc = (pos % CPR) ^ tile_swz(r);
+      const int lc = (pos % CPR) ^ tile_swz<D>(r);
       __builtin_amdgcn_global_load_lds((const void*)(base + (r * D + lc * 8)),
                                        (__attribute__((address_space(3))) void*)(dst + blk * 512),
                                        16, 0, 0);
@@ -152,7 +170,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
       const int blk = j * NWAVES + wave;
       const int pos = blk * 64 + lane;
       const int r = pos / CPR;
-      const int lc = (pos % CPR) ^ tile_swz(r);
+      const int lc = (pos % CPR) ^ tile_swz<D>(r);
       const int row = min(r0 + r, rlimit - 1);
       __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * D + lc * 8),
                                        (__attribute__((address_space(3))) void*)(dst + blk * 512),
@@ -161,28 +179,102 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
   }
 }
 
-// Element offsets, within a swizzled [*, D] tile, of the b128 row read that
-// feeds MFMA A-row n of a 32-row block (physical row swap23(n)) with logical
-// chunk 2c + g, for c = 0..3; chunk c >= 4 adds 64 * (c / 4) elements.
-template <int D>
-__device__ __forceinline__ void row_read_offsets(int n, int g, int* off) {
-  const int h = (2 * (n & 3)) | ((n >> 2) & 1);  // tile_swz(swap23(n))
-#pragma unroll
-  for (int c = 0; c < 4; ++c) off[c] = swap23(n) * D + 8 * ((2 * c + g) ^ h);
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, 32-bit data
+// format word), for loads whose address is a scalar base plus a 32-bit
+// per-lane offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Element offsets for tr_col8 on a swizzled [*, D] tile when the 8-row group
-// starts at a row base + 8g (base a multiple of 16): logical column block
-// db (32 columns) with db even (off[0]) or odd (off[1]); block db adds
-// 64 * (db / 2) elements.
+// The transfer of dma_tile through a buffer resource whose range is the
+// whole [rows, D] matrix: the per-lane byte offsets are computed once and a
+// tile costs one scalar offset.  Rows at or beyond `rows` fall outside the
+// range; the hardware returns zeros for them, so a ragged last tile arrives
+// zero-padded.
+template <int D, int ROWS, int NWAVES>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int NJ = ROWS * D / 512 / NWAVES;
+  static_assert((ROWS * D / 512) % NWAVES == 0, "tile must split evenly over the waves");
+  int voff[NJ];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int pos = (j * NWAVES + wave) * 64 + lane;
+      const int r = pos / CPR;
+      const int lc = (pos % CPR) ^ tile_swz<D>(r);
+      voff[j] = (r * D + lc * 8) * 2;
+    }
+  }
+  // Rows r0 .. r0+ROWS-1 of the [rows, D] bf16 matrix at `src` into `dst`.
+  __device__ __forceinline__ void load(const uint16_t* src, int rows, uint16_t* dst, int r0,
+                                       int wave) const {
+    const rsrc_t rs = make_rsrc(src, (uint32_t)rows * D * 2);
+    const int soff = (int)((uint32_t)r0 * D * 2);   // byte offset, may pass 2^31
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // (a local copy: passing voff[j] straight to the builtin makes the
+      // host pass drop the launch stubs of some kernel instantiations)
+      const int vo = voff[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (j * NWAVES + wave) * 512), 16, vo,
+          soff, 0, 0);
+    }
+  }
+};
+
+// Per-lane element offsets into a swizzled [*, D] tile.  The XOR group is 16
+// chunks (128 elements), so D = 256 keeps the offsets of its first 128
+// columns in registers and adds 128 for the rest.
+template <int D>
+constexpr int kRowOffs = D >= 256 ? 8 : D / 16;
+template <int D>
+constexpr int kTrOffs = D >= 256 ? 4 : D / 32;
+
+// b128 row read that feeds MFMA A-row n of a 32-row block (physical row
+// swap23(n)) with logical chunk 2c + g, i.e. k-step c of a contraction over
+// the D columns (c = 0 .. D/16-1): offset row_off<D>(off, c).
+template <int D>
+__device__ __forceinline__ void row_read_offsets(int n, int g, int* off) {
+  const int r = swap23(n);
+  const int h = tile_swz<D>(r);
+#pragma unroll
+  for (int c = 0; c < kRowOffs<D>; ++c) off[c] = r * D + 8 * ((2 * c + g) ^ h);
+}
+template <int D>
+__device__ __forceinline__ int row_off(const int* off, int c) {
+  return off[c % kRowOffs<D>] + 128 * (c / kRowOffs<D>);
+}
+
+// Transpose reads of 32-column block db (db = 0 .. D/32-1) for rows
+// 8*(lane/32) + (lane/4)%4 of a 16-row group: lane l supplies 4 bf16 at
+// logical chunk 4db + 2*((l/16)%2) + (l/2)%2, element 4*(l%2).
 template <int D>
 __device__ __forceinline__ void tr_read_offsets(int lane, int* off) {
   const int g = lane >> 5;
-  const int vr = (lane >> 2) & 3;
-  const int h = (2 * vr) | g;
+  const int r = 8 * g + ((lane >> 2) & 3);
+  const int h = tile_swz<D>(r);
   const int lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) off[p] = (8 * g + vr) * D + 8 * ((4 * p + lc) ^ h) + 4 * (lane & 1);
+  for (int db = 0; db < kTrOffs<D>; ++db) off[db] = r * D + 8 * ((4 * db + lc) ^ h) + 4 * (lane & 1);
+}
+template <int D>
+__device__ __forceinline__ int tr_off(const int* off, int db) {
+  return off[db % kTrOffs<D>] + 128 * (db / kTrOffs<D>);
+}
+
+// k-operand of a 32x32x16 MFMA contracted over 8 consecutive ROWS of a
+// swizzled tile: lane l gets rows 8*(l/32) .. +7 below `rows` (a 16-row
+// aligned position in the tile) of column 32*db + l%32.
+template <int D>
+__device__ __forceinline__ u32x4 tr_col8(const uint16_t* rows, const int* off, int db) {
+  constexpr int X = D >= 128 ? 2 : 1;   // rows + 4: the swizzle's top bit flips
+  const u32x2 a = lds_tr4(rows + tr_off<D>(off, db));
+  const u32x2 b = lds_tr4(rows + tr_off<D>(off, db ^ X) + 4 * D);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

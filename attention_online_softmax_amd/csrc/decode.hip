@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
 
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float c2 = fabsf(scale_log2);
-  int r_off[4], t_off[2];
+  int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
-      s = mfma32(*(const u32x4*)(cK + r_off[c & 3] + 64 * (c >> 2)), qreg[c] ^ qsign, s);
+      s = mfma32(*(const u32x4*)(cK + row_off<D>(r_off, c)), qreg[c] ^ qsign, s);
     const int kvalid = cur.L - tile_of(cur, t) * TK;  // keys of this tile that exist
     float rmax = kNegInf;
 #pragma unroll
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma32(tr_col8(cV + 16 * c * D + t_off[db & 1] + 64 * (db >> 1), D), pb[c],
+        oacc[db] = mfma32(tr_col8<D>(cV + 16 * c * D, t_off, db), pb[c],
                           oacc[db]);
 
     if (unit_end) {

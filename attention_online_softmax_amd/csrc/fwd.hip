@@ -128,11 +128,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // V tile through LDS transpose reads.  The accumulator O^T is again indexed
 // by the lane's query, so rescaling by alpha is a per-lane scalar.
 //
-// K/V tiles go from HBM straight into LDS with global_load_lds (no staging
-// registers), double-buffered: tile j+1 is in flight while tile j is used.
-// Tiles are dense [BC][D] with 16-byte chunks XOR-swizzled per row
-// (tile_swz) so that the K row reads and the V transpose reads are free of
-// bank conflicts.
+// K/V tiles of 32 keys go from HBM straight into LDS with buffer loads to
+// LDS (no staging registers) through a ring of four buffers per tensor, each
+// tile requested three loop bodies before its use; the loop body itself is
+// software-pipelined (see below).  Tiles are dense [32][D] with 16-byte
+// chunks XOR-swizzled per row (tile_swz) so that the K row reads and the V
+// transpose reads are free of bank conflicts.
 //
 // Normalisation reference: the exponentials are taken relative to a per-row
 // reference m_ref that only advances when the row maximum exceeds it by more
@@ -143,28 +144,27 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.f;
 
-template <int D>
-struct FwdTile {
-  static constexpr int BC = 64;  // keys per LDS tile
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, int n_qtiles) {
   constexpr int BR = 128;
-  constexpr int BC = FwdTile<D>::BC;
+  constexpr int BC = 32;         // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
-  // Two buffers per tensor as separate variables: the compiler can then see
-  // that the DMA into one buffer does not alias the reads of the other and
-  // does not wait for the DMA before those reads.
+  // Rings of four tile buffers per tensor, as separate variables: the
+  // compiler can then see which buffer each transfer writes and each read
+  // reads, and does not wait for unrelated transfers before a read.
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK2[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK3[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV2[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV3[BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -175,21 +175,22 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
   const int off = Skv - Sq;
-  const int wave_row0 = qtile * BR + wave * 32;
-  const int row = wave_row0 + n;
+  const int q0 = qtile * BR;
+  const int row = q0 + wave * 32 + n;
   const bool valid = row < Sq;
 
   const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
+  TileDma<D, BC, 4> dma;
+  dma.init(wave, lane);
 
-  const int last_row = min(qtile * BR + BR, Sq) - 1;
+  const int last_row = min(q0 + BR, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
-
-  // Start the first tile's transfer before anything else.
-  dma_tile<D, BC, 4>(Kh, sK0, 0, Skv, wave, lane);
-  dma_tile<D, BC, 4>(Vh, sV0, 0, Skv, wave, lane);
+  // Tiles before t_mask are fully visible to every row of the workgroup.
+  int t_mask = Skv / BC;
+  if (CAUSAL) t_mask = min(t_mask, (q0 + off + 1) / BC);
 
   // A negative scale is applied as |scale| on -Q (bf16 negation is exact),
   // so the maximum can be taken on raw scores and scaled afterwards.
@@ -202,6 +203,18 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
     qreg[c] ^= qsign;
   }
+  // Tile transfers, in the order the pipeline below counts on: K(0), K(1),
+  // then (K(2), V(0)), (K(3), V(1)).  Every transfer is issued even past the
+  // last tile: rows beyond Skv arrive as zeros, so the number of transfers
+  // in flight is the same in every loop body.
+  dma.load(Kh, Skv, sK0, 0, wave);
+  dma.load(Kh, Skv, sK1, BC, wave);
+  dma.load(Kh, Skv, sK2, 2 * BC, wave);
+  dma.load(Vh, Skv, sV0, 0, wave);
+  dma.load(Kh, Skv, sK3, 3 * BC, wave);
+  dma.load(Vh, Skv, sV1, BC, wave);
+  constexpr int kTileOps = TileDma<D, BC, 4>::NJ;   // transfer instructions per tile and wave
+
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -209,18 +222,16 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [0, row_limit)
-  // Last key any row of this wave may see (tiles beyond it are skipped).
-  const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
 
   // Per-lane LDS offsets (elements) into the swizzled tiles.
-  int k_off[4], v_off[2];
+  int k_off[kRowOffs<D>], v_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, k_off);
   tr_read_offsets<D>(lane, v_off);
 
   float m_ref = kNegInf, lpart = 0.f;
 
-  auto tile = [&](const uint16_t* cK, const uint16_t* cV, int k0, bool need_mask) {
-    f32x16 s[NKB];
+  // S^T(tile) = K(tile) Q^T for this wave's 32 queries.
+  auto qk = [&](const uint16_t* cK, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -229,34 +240,36 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma32(*(const u32x4*)(cK + kb * 32 * D + k_off[c & 3] + 64 * (c >> 2)),
+        s[kb] = mfma32(*(const u32x4*)(cK + kb * 32 * D + row_off<D>(k_off, c)),
                        qreg[c], s[kb]);
-    if (need_mask) {
+  };
+  // Scores of keys at or beyond the row's limit become -inf.
+  auto mask = [&](f32x16* s, int k0) {
+    const int lim = row_limit - k0 - 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-          s[kb][i] = (key < row_limit) ? s[kb][i] : kNegInf;
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kb * 32 + 16 * (i >> 3) + (i & 7);
+        s[kb][i] = (kk < lim) ? s[kb][i] : kNegInf;
+      }
+  };
+  // One tile of the online softmax: advance the reference if the tile's
+  // maximum passes it by more than kLazy, fold the tile's exponentials into
+  // lpart and pack them as the B operand of the PV product.  Returns the
+  // factor by which o must be rescaled (1 unless the reference moved).
+  auto softmax = [&](const f32x16* s, u32x4 (*pb)[2]) {
     float rmax = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[kb][i]);
     const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
-    if (__any(mnew > m_ref + kLazy)) {
-      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
-      lpart *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_ref = mnew;
-    }
+    const bool up = mnew > m_ref + kLazy;
+    const float alpha = up ? fast_exp2(m_ref - mnew) : 1.f;
+    m_ref = up ? mnew : m_ref;
     const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
-    u32x4 pb[NKB][2];
+    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -265,39 +278,96 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2, -msub));
           const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2, -msub));
-          lpart += p0 + p1;
+          lsum += p0 + p1;
           pb[kb][c][j] = pack_bf16x2(p0, p1);
         }
+    lpart = fmaf(lpart, alpha, lsum);
+    return alpha;
+  };
+  // O^T += V(tile)^T P^T.
+  auto pv = [&](const uint16_t* cV, const u32x4 (*pb)[2]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint16_t* vp = cV + (kb * 32 + 16 * c) * D + v_off[db & 1] + 64 * (db >> 1);
-          oacc[db] = mfma32(tr_col8(vp, D), pb[kb][c], oacc[db]);
+          oacc[db] = mfma32(tr_col8<D>(cV + (kb * 32 + 16 * c) * D, v_off, db), pb[kb][c],
+                            oacc[db]);
         }
   };
 
-  // One tile step: wait for tile tt, start tile tt+1 into the other buffer,
-  // then use tile tt.
-  auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV, int tt) {
-    const int k0 = tt * BC;
-    wait_vmcnt0();      // this wave's part of tile tt has landed in LDS
-    __syncthreads();    // ... and every wave's; the other buffer is free
-    if (tt + 1 < n_tiles) {
-      dma_tile<D, BC, 4>(Kh, nK, k0 + BC, Skv, wave, lane);
-      dma_tile<D, BC, 4>(Vh, nV, k0 + BC, Skv, wave, lane);
-    }
-    if (k0 <= wave_kv_last) {
-      const bool need_mask = (k0 + BC > Skv) || (CAUSAL && k0 + BC - 1 > wave_row0 + off);
-      tile(cK, cV, k0, need_mask);
+  // Software pipeline.  Tile j's scores S(j), its probabilities P(j) and
+  // its contribution P(j) V(j) are produced in three different loop
+  // bodies, so each body issues matrix products that do not depend on the
+  // softmax it computes: body j issues O += P(j) V(j) and S(j+2) on the
+  // matrix cores while the vector ALUs turn S(j+1) into P(j+1).
+  // K(t) lives in sK[t % 4] and V(t) in sV[t % 4].  Body j reads K(j+2) and
+  // V(j) and starts the transfers of K(j+5) and V(j+3) into the buffers
+  // that body j-1 read, so every tile is requested three bodies before use.
+  f32x16 s0[NKB], s1[NKB];
+  u32x4 p0[NKB][2], p1[NKB][2];
+
+  wait_vmcnt<4 * kTileOps>();   // K(0), K(1) have landed
+  __syncthreads();
+  qk(sK0, s0);
+  if (t_mask == 0) mask(s0, 0);
+  softmax(s0, p0);   // o is still zero: nothing to rescale
+  __syncthreads();   // every wave is done with K(0)
+  dma.load(Kh, Skv, sK0, 4 * BC, wave);
+  dma.load(Vh, Skv, sV2, 2 * BC, wave);
+  qk(sK1, s0);       // S(1); unused when there is one tile
+
+  auto body = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV,
+                  f32x16* sc, const u32x4 (*pc)[2], f32x16* sn, u32x4 (*pn)[2]) {
+    wait_vmcnt<4 * kTileOps>();   // this wave's part of K(j+2) and V(j) has landed
+    lds_barrier();     // ... and every wave's; K(j+1), V(j-1) are no longer read
+    dma.load(Kh, Skv, nK, (j + 5) * BC, wave);
+    dma.load(Vh, Skv, nV, (j + 3) * BC, wave);
+    if (j + 1 >= t_mask) mask(sc, (j + 1) * BC);
+    pv(cV, pc);
+    // S(j+2); in the last body this is past the last tile and is discarded.
+    qk(cK, sn);
+    const float alpha = softmax(sc, pn);
+    // P(j+1) is computed here, not next to its use in the next body.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(pn[kb][c]));
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
   };
+  const int n_bodies = n_tiles - 1;
+  int j = 0;
 #pragma clang loop unroll(disable)
-  for (int tt = 0; tt < n_tiles; tt += 2) {
-    step(sK0, sV0, sK1, sV1, tt);
-    if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
+  for (; j + 4 <= n_bodies; j += 4) {
+    body(j, sK2, sV0, sK1, sV3, s0, p0, s1, p1);
+    body(j + 1, sK3, sV1, sK2, sV0, s1, p1, s0, p0);
+    body(j + 2, sK0, sV2, sK3, sV1, s0, p0, s1, p1);
+    body(j + 3, sK1, sV3, sK0, sV2, s1, p1, s0, p0);
+  }
+  if (j < n_bodies) {
+    body(j, sK2, sV0, sK1, sV3, s0, p0, s1, p1);
+    if (++j < n_bodies) {
+      body(j, sK3, sV1, sK2, sV0, s1, p1, s0, p0);
+      if (++j < n_bodies) {
+        body(j, sK0, sV2, sK3, sV1, s0, p0, s1, p1);
+        ++j;
+      }
+    }
+  }
+  // j == n_tiles - 1: P(j) is in register set j % 2 and V(j) in sV[j % 4].
+  wait_vmcnt0();
+  __syncthreads();
+  switch (j & 3) {
+    case 0: pv(sV0, p0); break;
+    case 1: pv(sV1, p1); break;
+    case 2: pv(sV2, p0); break;
+    default: pv(sV3, p1); break;
   }
 
   const float l = halfwave_sum(lpart);
