@@ -165,7 +165,8 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0) return 0;
-  return round256(2 * (size_t)B * Hq * Sq * sizeof(float));
+  const size_t sqp = ((size_t)Sq + 31) / 32 * 32;
+  return round256(2 * (size_t)B * Hq * sqp * sizeof(float));
 }
 
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,

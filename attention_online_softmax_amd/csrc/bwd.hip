@@ -14,6 +14,8 @@
 // atomics.  Both product kernels stream their tiles HBM -> LDS with
 // global_load_lds into double-buffered, swizzled tiles (see common.h) that
 // are read both by rows and, through transpose reads, by columns.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -21,19 +23,26 @@ namespace attn {
 
 // ---------------------------------------------------------------------------
 // Per query row: D_i = sum_c dO[i, c] * O[i, c] and nl_i = -LSE_i * log2(e),
-// both fp32, written to the workspace as [D (rows)] [nl (rows)].
+// both fp32, written to the workspace as [D (rows)] [nl (rows)] with each
+// head's rows padded to Sqp = Sq rounded up to 32; padding rows get D = 0
+// and nl = -inf, so their probabilities are exactly 0.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
                                                            const float* __restrict__ LSE,
-                                                           float* __restrict__ ws, int64_t rows) {
+                                                           float* __restrict__ ws, int Sq, int Sqp,
+                                                           int64_t rows_pad) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int64_t prow = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // padded row
   const int sub = threadIdx.x % LPR;
+  const int64_t bh = prow / Sqp;
+  const int q = (int)(prow - bh * Sqp);
+  const bool real = prow < rows_pad && q < Sq;
+  const int64_t row = bh * Sq + q;
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const u32x4 o = *(const u32x4*)(O + row * D + sub * 8);
     const u32x4 g = *(const u32x4*)(dO + row * D + sub * 8);
 #pragma unroll
@@ -44,9 +53,9 @@ __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __res
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
-  if (row < rows && sub == 0) {
-    ws[row] = acc;
-    ws[rows + row] = -LSE[row] * kLog2e;
+  if (prow < rows_pad && sub == 0) {
+    ws[prow] = acc;
+    ws[rows_pad + prow] = real ? -LSE[row] * kLog2e : kNegInf;
   }
 }
 
@@ -70,35 +79,37 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 // dK, dV: one workgroup per (b, key/value head, 128-key tile); each of its
 // four waves owns 32 keys, holding their K and V rows in registers (the
 // B operands of S = Q K^T and dP = dO V^T) and their dK^T, dV^T accumulators.
-// Query tiles of 64 rows of Q and dO, plus D and nl for those rows, stream
-// through LDS.  Per 32-query sub-block, Q and dO rows are fed to the MFMA in
-// swap23 order, so each lane (one key) holds P and dS for 8 contiguous
-// queries per k-step: the B operands of dV^T += dO^T P and dK^T += Q^T dS,
-// whose A operands dO^T and Q^T come from transpose reads of the same tiles.
+// Query tiles of 32 rows of Q and dO, plus D and nl of those rows, stream
+// through a ring of four LDS slots (rows past Sq arrive as zeros; their nl
+// is -inf).  Q and dO rows are fed to the MFMA in swap23 order, so each lane
+// (one key) holds P and dS for 8 contiguous queries per k-step: the
+// B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands dO^T and
+// Q^T come from transpose reads of the same tiles.
+//
+// Software pipeline over the query tiles i of all query heads of the group:
+// body i issues dV^T, dK^T += ...(i-1) and S(i+1), dP(i+1) on the matrix
+// cores while the vector ALUs turn S(i), dP(i) into P(i), dS(i); the body
+// has no branch between them, so the two can be interleaved.  Tile t lives
+// in slot t % 4; body i reads tiles i-1, i, i+1 and starts the transfer of
+// tile i+2 into the slot of tile i-2.
 // ---------------------------------------------------------------------------
-template <int D>
-struct BwdTile {
-  static constexpr int QB = 64;   // query rows per LDS tile (dK/dV)
-  static constexpr int KB = 64;   // key rows per LDS tile (dQ)
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Skv, float scale,
-    float scale_log2, int64_t rows_total) {
-  constexpr int QB = BwdTile<D>::QB;
+    uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale,
+    float scale_log2, int64_t rows_pad) {
+  constexpr int QT = 32;   // query rows per tile
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  // Double buffers as separate variables (see the forward kernel): the DMA
-  // into one buffer is then known not to alias the reads of the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QB * D];
-  __shared__ __attribute__((aligned(16))) float sDn0[2 * QB];   // D then nl
-  __shared__ __attribute__((aligned(16))) float sDn1[2 * QB];
+  // Slot: Q tile, dO tile, then D and nl of its rows (2 x QT floats).  One
+  // variable per slot: the compiler tracks transfers into LDS per variable
+  // and so never waits for the transfer into one slot before reading another.
+  constexpr int SLOT = 2 * QT * D + 4 * QT;
+  __shared__ __attribute__((aligned(1024))) uint16_t sT0[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sT1[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sT2[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sT3[SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -114,31 +125,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
-  const float* Dd = ws;
-  const float* NL = ws + rows_total;
 
   // Queries that can see any key of this tile: i >= first_key - off.
-  const int q_begin = CAUSAL ? max(0, ktile * 128 - off) : 0;
-  const int q_start = (q_begin / QB) * QB;
-  const int n_qt = (Sq - q_start + QB - 1) / QB;  // query tiles per head
+  const int q_start = CAUSAL ? (max(0, ktile * 128 - off) / QT) * QT : 0;
+  const int n_qt = (Sq - q_start + QT - 1) / QT;   // query tiles per head (>= 1)
   const int n_it = G * n_qt;
-
-  auto issue = [&](int it, uint16_t* dQt, uint16_t* dGt, float* dDn) {
-    const int hh = it / n_qt;
-    const int q0 = q_start + (it % n_qt) * QB;
-    const int64_t bh = (int64_t)b * Hq + hk * G + hh;
-    dma_tile<D, QB, 4>(Q + bh * Sq * D, dQt, q0, Sq, wave, lane);
-    dma_tile<D, QB, 4>(dO + bh * Sq * D, dGt, q0, Sq, wave, lane);
-    if (wave < 2) {
-      // wave 0: D of rows q0 .. q0+63, wave 1: nl of those rows, one float
-      // per lane (rows past Sq repeat row Sq-1; they are masked).
-      const float* src = (wave == 0 ? Dd : NL) + bh * Sq + min(q0 + lane, Sq - 1);
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)&dDn[wave * QB],
-                                       4, 0, 0);
-    }
-  };
-  issue(0, sQ0, sG0, sDn0);
 
   u32x4 kreg[NDC], vreg[NDC];
   const int krow = min(key, Skv - 1);
@@ -147,6 +138,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     kreg[c] = *(const u32x4*)(Kh + (int64_t)krow * D + c * 16 + 8 * g);
     vreg[c] = *(const u32x4*)(Vh + (int64_t)krow * D + c * 16 + 8 * g);
   }
+
+  TileDma<D, QT, 4> dma;
+  dma.init(wave, lane);
+  // Transfer of the next iteration tile (query head dma_hh, query tile
+  // dma_qt) into `slot`; past the last tile nothing is fetched.  D and nl:
+  // one float per lane of wave 0 (lanes 0..31 D, 32..63 nl).
+  int dma_hh = 0, dma_qt = 0;
+  auto issue = [&](uint16_t* slot) {
+    if (dma_hh >= G) return;
+    const int q0 = q_start + dma_qt * QT;
+    const int64_t bh = (int64_t)b * Hq + hk * G + dma_hh;
+    dma.load(Q + bh * Sq * D, Sq, slot, q0, wave);
+    dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, wave);
+    if (wave == 0) {
+      const float* src = ws + (g ? rows_pad : 0) + bh * Sqp + q0 + n;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, 0, 0);
+    }
+    if (++dma_qt == n_qt) {
+      dma_qt = 0;
+      ++dma_hh;
+    }
+  };
+  issue(sT0);
+  issue(sT1);
+
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -157,82 +174,148 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
-  auto step = [&](const uint16_t* cQ, const uint16_t* cG, const float* cDn, uint16_t* nQ,
-                  uint16_t* nG, float* nDn, int it) {
-    const int q0 = q_start + (it % n_qt) * QB;
-    wait_vmcnt0();
-    __syncthreads();
-    if (it + 1 < n_it) issue(it + 1, nQ, nG, nDn);
+  // S = Q K^T and dP = dO V^T of one tile (element i: query
+  // 16*(i/8) + 8g + i%8 of the tile, key `key`).
+  auto sdp = [&](const uint16_t* slot, f32x16& s, f32x16& dp) {
+    const uint16_t* cQ = slot;
+    const uint16_t* cG = slot + QT * D;
 #pragma unroll
-    for (int sb = 0; sb < QB / 32; ++sb) {
-      const int qs = q0 + sb * 32;
-      // Sub-block fully hidden from this wave's keys: skip.
-      if (CAUSAL && key0_wave > qs + 31 + off) continue;
-      if (qs >= Sq) continue;
-      // Queries past Sq read a repeated row and must not contribute; keys
-      // past Skv only affect their own (unstored) dK/dV columns.
-      const bool need_mask = (qs + 32 > Sq) || (CAUSAL && key0_wave + 31 > qs + off);
-      f32x16 s, dp;
+    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      const uint16_t* qb = cQ + sb * 32 * D;
-      const uint16_t* gb = cG + sb * 32 * D;
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        const int o = row_off<D>(r_off, c);
-        s = mfma32(*(const u32x4*)(qb + o), kreg[c], s);
-        dp = mfma32(*(const u32x4*)(gb + o), vreg[c], dp);
-      }
-      // Element i is query qs + 16*(i/8) + 8g + i%8 against key `key`.
-      const float* dn = cDn + sb * 32;
-      u32x4 pb[2], dsb[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const f32x4 d0 = *(const f32x4*)(dn + 16 * c + 8 * g);
-        const f32x4 d1 = *(const f32x4*)(dn + 16 * c + 8 * g + 4);
-        const f32x4 l0 = *(const f32x4*)(dn + QB + 16 * c + 8 * g);
-        const f32x4 l1 = *(const f32x4*)(dn + QB + 16 * c + 8 * g + 4);
-        float pv[8], dsv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * c + j;
-          const float nl = j < 4 ? l0[j] : l1[j - 4];
-          const float dd = j < 4 ? d0[j] : d1[j - 4];
-          float p = fast_exp2(fmaf(s[i], scale_log2, nl));
-          if (need_mask) {
-            const int qi = qs + 16 * c + 8 * g + j;
-            const bool ok = (qi < Sq) && (!CAUSAL || key <= qi + off);
-            p = ok ? p : 0.f;
-          }
-          pv[j] = p;
-          dsv[j] = p * (dp[i] - dd);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pb[c][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-          dsb[c][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
-        }
-      }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (contracted over the 32 queries).
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvt[db] = mfma32(tr_col8<D>(gb + 16 * c * D, t_off, db), pb[c], dvt[db]);
-          dkt[db] = mfma32(tr_col8<D>(qb + 16 * c * D, t_off, db), dsb[c], dkt[db]);
-        }
+    for (int c = 0; c < NDC; ++c) {
+      const int o = row_off<D>(r_off, c);
+      s = mfma32(*(const u32x4*)(cQ + o), kreg[c], s);
+      dp = mfma32(*(const u32x4*)(cG + o), vreg[c], dp);
     }
   };
+  // P = exp(scale S - LSE) and dS = P (dP - D) of the tile starting at
+  // query qs, packed as the B operands of the dV and dK products.  Rows
+  // past Sq have nl = -inf; with a causal mask, query qi sees key `key`
+  // iff key <= qi + off, applied by replacing nl with -inf (no branch).
+  auto pds = [&](const f32x16& s, const f32x16& dp, const uint16_t* slot, int qs, u32x4* pb,
+                 u32x4* dsb) {
+    const float* cN = (const float*)(slot + 2 * QT * D);
+    const int lo = key - off - qs - 8 * g;   // element (c, j) is visible iff 16c + j >= lo
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 d0 = *(const f32x4*)(cN + 16 * c + 8 * g);
+      const f32x4 d1 = *(const f32x4*)(cN + 16 * c + 8 * g + 4);
+      const f32x4 l0 = *(const f32x4*)(cN + QT + 16 * c + 8 * g);
+      const f32x4 l1 = *(const f32x4*)(cN + QT + 16 * c + 8 * g + 4);
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * c + j;
+        float nl = j < 4 ? l0[j] : l1[j - 4];
+        const float dd = j < 4 ? d0[j] : d1[j - 4];
+        if (CAUSAL) nl = (16 * c + j >= lo) ? nl : kNegInf;
+        const float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+        pv[j] = p;
+        dsv[j] = p * (dp[i] - dd);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pb[c][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        dsb[c][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
+      }
+    }
+  };
+  int cur_qt = 0;   // query tile of the next softmax step
+  auto next_qs = [&]() {
+    const int qs = q_start + cur_qt * QT;
+    if (++cur_qt == n_qt) cur_qt = 0;
+    return qs;
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dS  (contracted over the tile's queries).
+  auto dkdv = [&](const uint16_t* slot, const u32x4* pb, const u32x4* dsb) {
+    const uint16_t* cQ = slot;
+    const uint16_t* cG = slot + QT * D;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvt[db] = mfma32(tr_col8<D>(cG + 16 * c * D, t_off, db), pb[c], dvt[db]);
+        dkt[db] = mfma32(tr_col8<D>(cQ + 16 * c * D, t_off, db), dsb[c], dkt[db]);
+      }
+  };
+
+  f32x16 s0, dp0, s1, dp1;
+  u32x4 pb0[2], ds0[2], pb1[2], ds1[2];
+
+  wait_vmcnt0();   // K, V rows and tiles 0, 1 have landed
+  lds_barrier();
+  issue(sT2);
+  sdp(sT0, s0, dp0);
+  pds(s0, dp0, sT0, next_qs(), pb0, ds0);
+  sdp(sT1, s1, dp1);   // unused when there is one tile
+
+  // Body i: tiles i-1 (products), i (softmax), i+1 (S, dP) in slots tPr,
+  // tCu, tNx; the transfer of tile i+2 goes to slot tNw.
+  auto body = [&](const uint16_t* tPr, const uint16_t* tCu, const uint16_t* tNx, uint16_t* tNw,
+                  const f32x16& sCu, const f32x16& dpCu, f32x16& sNx, f32x16& dpNx,
+                  const u32x4* pbPr, const u32x4* dsPr, u32x4* pbCu, u32x4* dsCu) {
+    wait_vmcnt0();   // this wave's part of tile i+1 has landed
+    lds_barrier();   // ... and every wave's; nobody reads tile i-2 any more
+    issue(tNw);
+    const int qs = next_qs();
+    dkdv(tPr, pbPr, dsPr);
+    sdp(tNx, sNx, dpNx);   // past the last tile this reads a stale slot and is unused
+    pds(sCu, dpCu, tCu, qs, pbCu, dsCu);
+    // Issue order: LDS reads a few products ahead; each product followed
+    // by the reads of a later one and a share of the softmax step.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int k = 0; k < 4 * NDB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * NDC; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    // P(i), dS(i) are computed here, not next to their use in body i+1 (one
+    // statement: each asm statement ends a scheduling region).
+    asm volatile("" ::"v"(pbCu[0]), "v"(pbCu[1]), "v"(dsCu[0]), "v"(dsCu[1]));
+  };
+  int i = 1;
 #pragma clang loop unroll(disable)
-  for (int it = 0; it < n_it; it += 2) {
-    step(sQ0, sG0, sDn0, sQ1, sG1, sDn1, it);
-    if (it + 1 < n_it) step(sQ1, sG1, sDn1, sQ0, sG0, sDn0, it + 1);
+  for (; i + 4 <= n_it; i += 4) {
+    body(sT0, sT1, sT2, sT3, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
+    body(sT1, sT2, sT3, sT0, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
+    body(sT2, sT3, sT0, sT1, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
+    body(sT3, sT0, sT1, sT2, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
+  }
+  if (i < n_it) {
+    body(sT0, sT1, sT2, sT3, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
+    if (++i < n_it) {
+      body(sT1, sT2, sT3, sT0, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
+      if (++i < n_it) {
+        body(sT2, sT3, sT0, sT1, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
+        ++i;
+      }
+    }
+  }
+  // The products of tile n_it-1 (slot (n_it-1) % 4, register set
+  // (n_it-1) % 2) remain; its data landed before body n_it-2 read it.
+  switch ((n_it - 1) & 3) {
+    case 0: dkdv(sT0, pb0, ds0); break;
+    case 1: dkdv(sT1, pb1, ds1); break;
+    case 2: dkdv(sT2, pb0, ds0); break;
+    default: dkdv(sT3, pb1, ds1); break;
   }
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
   store_transposed<NDB>(dK + kro, dkt, g, scale);
   store_transposed<NDB>(dV + kro, dvt, g, 1.f);
 }
+
+template <int D>
+struct BwdTile {
+  static constexpr int KB = 64;   // key rows per LDS tile (dQ)
+};
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, query head, 128-query tile), 32 queries per wave
@@ -245,8 +328,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dQ,
-    int BH, int Hq, int Hkv, int Sq, int Skv, float scale, float scale_log2, int n_qtiles,
-    int64_t rows_total) {
+    int BH, int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale, float scale_log2,
+    int n_qtiles, int64_t rows_pad) {
   constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -286,8 +369,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     qreg[c] = *(const u32x4*)(Qr + c * 16 + 8 * g);
     greg[c] = *(const u32x4*)(dOr + c * 16 + 8 * g);
   }
-  const float dd = ws[(int64_t)bh * Sq + qrow];
-  const float nl = ws[rows_total + (int64_t)bh * Sq + qrow];
+  const float dd = ws[(int64_t)bh * Sqp + qrow];
+  const float nl = ws[rows_pad + (int64_t)bh * Sqp + qrow];
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -361,11 +444,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int Sqp = (a.Sq + 31) / 32 * 32;
+  const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
   constexpr int RPB = 256 / (D / 8);
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_dot_do_o_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, rows);
+  hipLaunchKernelGGL((bwd_dot_do_o_kernel<D>), dim3((rows_pad + RPB - 1) / RPB), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, a.Sq,
+                     Sqp, rows_pad);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -376,7 +461,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     BHk, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, sl2, rows);
+                     BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.scale, sl2, rows_pad);
   timing_mark(a.stream, 3);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -386,7 +471,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dq, BH, a.Hq, a.Hkv,
-                     a.Sq, a.Skv, a.scale, sl2, n_qtiles, rows);
+                     a.Sq, Sqp, a.Skv, a.scale, sl2, n_qtiles, rows_pad);
   timing_mark(a.stream, 5);
   return hipGetLastError();
 }

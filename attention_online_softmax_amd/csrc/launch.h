@@ -45,7 +45,7 @@ struct BwdArgs {
   void* dv;
   int B, Hq, Hkv, Sq, Skv, d, causal;
   float scale;
-  float* ws;  // [B, Hq, Sq] D = rowsum(dO * O), then [B, Hq, Sq] -LSE * log2(e)
+  float* ws;  // [B, Hq, Sqp] D = rowsum(dO * O), then [B, Hq, Sqp] -LSE * log2(e); Sqp = Sq rounded up to 32
   hipStream_t stream;
 };
 

@@ -129,9 +129,10 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         int B, int Hq, int Hkv, int Skv, int d, float scale, int n_splits,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace for attn_bwd: 2 * B * Hq * Sq float32 values (per query row
- * D_i = dO_i . O_i and -lse_i * log2(e)), rounded up to 256 bytes.  Returns
- * 0 for invalid sizes. */
+/* Workspace for attn_bwd: 2 * B * Hq * Sqp float32 values, Sqp = Sq rounded
+ * up to a multiple of 32 (per query row D_i = dO_i . O_i and
+ * -lse_i * log2(e), with rows past Sq padded), rounded up to 256 bytes.
+ * Returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
 
 /*
