@@ -131,15 +131,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Wait until at most N vector memory operations of this wave are in flight
-// (they complete in issue order, so everything older than the newest N has
-// landed).  gfx9 encoding: vmcnt in bits 3:0 and 15:14.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
 // This wave's share of the transfer of rows r0 .. r0+ROWS-1 of a row-major
 // [*, D] bf16 matrix (rows at or beyond rlimit read row rlimit-1 instead)
 // into the swizzled tile `dst`.  Each global_load_lds moves 64 chunks of 16

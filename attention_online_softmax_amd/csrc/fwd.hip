@@ -129,9 +129,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // by the lane's query, so rescaling by alpha is a per-lane scalar.
 //
 // K/V tiles of 32 keys go from HBM straight into LDS with buffer loads to
-// LDS (no staging registers) through a ring of four buffers per tensor, each
-// tile requested three loop bodies before its use; the loop body itself is
-// software-pipelined (see below).  Tiles are dense [32][D] with 16-byte
+// LDS (no staging registers), double-buffered: tile j+1 is requested when
+// tile j's loop body starts.  Tiles are dense [32][D] with 16-byte
 // chunks XOR-swizzled per row (tile_swz) so that the K row reads and the V
 // transpose reads are free of bank conflicts.
 //
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 constexpr float kLazy = 8.f;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, int n_qtiles) {
@@ -154,17 +153,13 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
-  // Rings of four tile buffers per tensor, as separate variables: the
-  // compiler can then see which buffer each transfer writes and each read
-  // reads, and does not wait for unrelated transfers before a read.
+  // Two tile buffers per tensor, as separate variables: the compiler can
+  // then see which buffer each transfer writes and each read reads, and
+  // does not wait for the transfer into one before reading the other.
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK2[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK3[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV2[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV3[BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -203,17 +198,8 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
     qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
     qreg[c] ^= qsign;
   }
-  // Tile transfers, in the order the pipeline below counts on: K(0), K(1),
-  // then (K(2), V(0)), (K(3), V(1)).  Every transfer is issued even past the
-  // last tile: rows beyond Skv arrive as zeros, so the number of transfers
-  // in flight is the same in every loop body.
   dma.load(Kh, Skv, sK0, 0, wave);
-  dma.load(Kh, Skv, sK1, BC, wave);
-  dma.load(Kh, Skv, sK2, 2 * BC, wave);
   dma.load(Vh, Skv, sV0, 0, wave);
-  dma.load(Kh, Skv, sK3, 3 * BC, wave);
-  dma.load(Vh, Skv, sV1, BC, wave);
-  constexpr int kTileOps = TileDma<D, BC, 4>::NJ;   // transfer instructions per tile and wave
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -297,77 +283,38 @@ __global__ __launch_bounds__(256, (D >= 256) ? 1 : 2) void fwd_bf16_kernel(
         }
   };
 
-  // Software pipeline.  Tile j's scores S(j), its probabilities P(j) and
-  // its contribution P(j) V(j) are produced in three different loop
-  // bodies, so each body issues matrix products that do not depend on the
-  // softmax it computes: body j issues O += P(j) V(j) and S(j+2) on the
-  // matrix cores while the vector ALUs turn S(j+1) into P(j+1).
-  // K(t) lives in sK[t % 4] and V(t) in sV[t % 4].  Body j reads K(j+2) and
-  // V(j) and starts the transfers of K(j+5) and V(j+3) into the buffers
-  // that body j-1 read, so every tile is requested three bodies before use.
-  f32x16 s0[NKB], s1[NKB];
-  u32x4 p0[NKB][2], p1[NKB][2];
-
-  wait_vmcnt<4 * kTileOps>();   // K(0), K(1) have landed
-  __syncthreads();
-  qk(sK0, s0);
-  if (t_mask == 0) mask(s0, 0);
-  softmax(s0, p0);   // o is still zero: nothing to rescale
-  __syncthreads();   // every wave is done with K(0)
-  dma.load(Kh, Skv, sK0, 4 * BC, wave);
-  dma.load(Vh, Skv, sV2, 2 * BC, wave);
-  qk(sK1, s0);       // S(1); unused when there is one tile
-
-  auto body = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV,
-                  f32x16* sc, const u32x4 (*pc)[2], f32x16* sn, u32x4 (*pn)[2]) {
-    wait_vmcnt<4 * kTileOps>();   // this wave's part of K(j+2) and V(j) has landed
-    lds_barrier();     // ... and every wave's; K(j+1), V(j-1) are no longer read
-    dma.load(Kh, Skv, nK, (j + 5) * BC, wave);
-    dma.load(Vh, Skv, nV, (j + 3) * BC, wave);
-    if (j + 1 >= t_mask) mask(sc, (j + 1) * BC);
-    pv(cV, pc);
-    // S(j+2); in the last body this is past the last tile and is discarded.
-    qk(cK, sn);
-    const float alpha = softmax(sc, pn);
-    // P(j+1) is computed here, not next to its use in the next body.
+  {
+    // Tile loop: wait for tile j, start tile j+1 into the other buffers,
+    // then S(j), softmax, O += P(j) V(j).  Two or more waves per SIMD (the
+    // register budget of every head dimension allows it) overlap the matrix
+    // products of one wave with the softmax and LDS latency of another.
+    // Tiles past the last key of this wave's rows are skipped.
+    const int wave_kv_last =
+        CAUSAL ? min(Skv, min(q0 + wave * 32 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
+    f32x16 s[NKB];
+    u32x4 p[NKB][2];
+    auto step = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
+      wait_vmcnt0();   // this wave's part of tile j has landed
+      lds_barrier();   // ... and every wave's; tile j-1 is no longer read
+      dma.load(Kh, Skv, nK, (j + 1) * BC, wave);
+      dma.load(Vh, Skv, nV, (j + 1) * BC, wave);
+      if (j * BC > wave_kv_last) return;
+      qk(cK, s);
+      if (j >= t_mask) mask(s, j * BC);
+      const float alpha = softmax(s, p);
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) asm volatile("" ::"v"(pn[kb][c]));
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-  };
-  const int n_bodies = n_tiles - 1;
-  int j = 0;
-#pragma clang loop unroll(disable)
-  for (; j + 4 <= n_bodies; j += 4) {
-    body(j, sK2, sV0, sK1, sV3, s0, p0, s1, p1);
-    body(j + 1, sK3, sV1, sK2, sV0, s1, p1, s0, p0);
-    body(j + 2, sK0, sV2, sK3, sV1, s0, p0, s1, p1);
-    body(j + 3, sK1, sV3, sK0, sV2, s1, p1, s0, p0);
-  }
-  if (j < n_bodies) {
-    body(j, sK2, sV0, sK1, sV3, s0, p0, s1, p1);
-    if (++j < n_bodies) {
-      body(j, sK3, sV1, sK2, sV0, s1, p1, s0, p0);
-      if (++j < n_bodies) {
-        body(j, sK0, sV2, sK3, sV1, s0, p0, s1, p1);
-        ++j;
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
+      pv(cV, p);
+    };
+#pragma clang loop unroll(disable)
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(j, sK0, sV0, sK1, sV1);
+      if (j + 1 < n_tiles) step(j + 1, sK1, sV1, sK0, sV0);
     }
-  }
-  // j == n_tiles - 1: P(j) is in register set j % 2 and V(j) in sV[j % 4].
-  wait_vmcnt0();
-  __syncthreads();
-  switch (j & 3) {
-    case 0: pv(sV0, p0); break;
-    case 1: pv(sV1, p1); break;
-    case 2: pv(sV2, p0); break;
-    default: pv(sV3, p1); break;
   }
 
   const float l = halfwave_sum(lpart);
@@ -407,7 +354,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0,
+                     a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e,
                      n_qtiles);
