@@ -178,6 +178,8 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  // The kernels address the workspace with 32-bit byte offsets.
+  if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
   if (!bwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   if (!workspace) return ATTN_ERR_WORKSPACE;

@@ -77,24 +77,20 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (b, key/value head, 128-key tile); each of its
-// four waves owns 32 keys, holding their K and V rows in registers (the
-// B operands of S = Q K^T and dP = dO V^T) and their dK^T, dV^T accumulators.
-// Query tiles of 32 rows of Q and dO, plus D and nl of those rows, stream
-// through a ring of four LDS slots (rows past Sq arrive as zeros; their nl
-// is -inf).  Q and dO rows are fed to the MFMA in swap23 order, so each lane
-// (one key) holds P and dS for 8 contiguous queries per k-step: the
-// B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands dO^T and
-// Q^T come from transpose reads of the same tiles.
-//
-// Software pipeline over the query tiles i of all query heads of the group:
-// body i issues dV^T, dK^T += ...(i-1) and S(i+1), dP(i+1) on the matrix
-// cores while the vector ALUs turn S(i), dP(i) into P(i), dS(i); the body
-// has no branch between them, so the two can be interleaved.  Tile t lives
-// in slot t % 4; body i reads tiles i-1, i, i+1 and starts the transfer of
-// tile i+2 into the slot of tile i-2.
+// four waves owns 32 keys and their dK^T, dV^T accumulators.  The K rows of
+// the wave's keys are held in registers (B operand of S = Q K^T); the V rows
+// of the workgroup's 128 keys sit in LDS for the whole kernel (B operand of
+// dP = dO V^T, read by rows), which keeps a wave within the 256 registers of
+// two waves per SIMD.  Query tiles of 32 rows of Q and dO, plus D and nl of
+// those rows, are double-buffered through LDS (rows past Sq arrive as zeros
+// and have nl = -inf).  Q and dO rows are fed to the MFMA in swap23 order, so
+// each lane (one key) holds P and dS for 8 contiguous queries per k-step:
+// the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands dO^T
+// and Q^T come from transpose reads of the same tiles.  The loop covers the
+// query tiles of all query heads of the group.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale,
@@ -103,13 +99,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   // Slot: Q tile, dO tile, then D and nl of its rows (2 x QT floats).  One
-  // variable per slot: the compiler tracks transfers into LDS per variable
-  // and so never waits for the transfer into one slot before reading another.
+  // variable per slot (and for V): the compiler tracks transfers into LDS
+  // per variable and so never waits for the transfer into one slot before
+  // reading another.
   constexpr int SLOT = 2 * QT * D + 4 * QT;
   __shared__ __attribute__((aligned(1024))) uint16_t sT0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint16_t sT1[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sT2[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sT3[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[128 * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -120,7 +116,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int G = Hq / Hkv;
   const int off = Skv - Sq;
   const int key0_wave = ktile * 128 + wave * 32;
-  const int key = key0_wave + n;
+  // Lane n owns key swap23(n) of the wave's 32: the V rows it needs as the
+  // B operand of dP are then read exactly like the Q and dO rows.
+  const int key = key0_wave + swap23(n);
   const bool kvalid = key < Skv;
 
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
@@ -131,19 +129,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int n_qt = (Sq - q_start + QT - 1) / QT;   // query tiles per head (>= 1)
   const int n_it = G * n_qt;
 
-  u32x4 kreg[NDC], vreg[NDC];
-  const int krow = min(key, Skv - 1);
-#pragma unroll
-  for (int c = 0; c < NDC; ++c) {
-    kreg[c] = *(const u32x4*)(Kh + (int64_t)krow * D + c * 16 + 8 * g);
-    vreg[c] = *(const u32x4*)(Vh + (int64_t)krow * D + c * 16 + 8 * g);
+  // The workgroup's V rows (rows past Skv arrive as zeros).
+  {
+    TileDma<D, 128, 4> vdma;
+    vdma.init(wave, lane);
+    vdma.load(Vh, Skv, sV, ktile * 128, wave);
   }
-
   TileDma<D, QT, 4> dma;
   dma.init(wave, lane);
+  // D and nl of a tile: one float per lane of wave 0 (lanes 0..31 D,
+  // 32..63 nl) through a descriptor over the whole workspace (< 4 GiB).
+  const rsrc_t ws_rs = make_rsrc(ws, (uint32_t)(2 * rows_pad * 4));
+  const uint32_t dn_lane = ((g ? (uint32_t)rows_pad : 0u) + n) * 4;
   // Transfer of the next iteration tile (query head dma_hh, query tile
-  // dma_qt) into `slot`; past the last tile nothing is fetched.  D and nl:
-  // one float per lane of wave 0 (lanes 0..31 D, 32..63 nl).
+  // dma_qt) into `slot`; past the last tile nothing is fetched.
   int dma_hh = 0, dma_qt = 0;
   auto issue = [&](uint16_t* slot) {
     if (dma_hh >= G) return;
@@ -151,18 +150,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int64_t bh = (int64_t)b * Hq + hk * G + dma_hh;
     dma.load(Q + bh * Sq * D, Sq, slot, q0, wave);
     dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, wave);
-    if (wave == 0) {
-      const float* src = ws + (g ? rows_pad : 0) + bh * Sqp + q0 + n;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, 0, 0);
-    }
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ws_rs, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, (int)dn_lane,
+          (int)((uint32_t)(bh * Sqp + q0) * 4), 0, 0);
     if (++dma_qt == n_qt) {
       dma_qt = 0;
       ++dma_hh;
     }
   };
   issue(sT0);
-  issue(sT1);
+
+  u32x4 kreg[NDC];
+  const int krow = min(key, Skv - 1);
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) kreg[c] = *(const u32x4*)(Kh + (int64_t)krow * D + c * 16 + 8 * g);
 
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -173,138 +175,81 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
+  const uint16_t* sVw = sV + wave * 32 * D;
 
-  // S = Q K^T and dP = dO V^T of one tile (element i: query
-  // 16*(i/8) + 8g + i%8 of the tile, key `key`).
-  auto sdp = [&](const uint16_t* slot, f32x16& s, f32x16& dp) {
+  // One tile: S = Q K^T and dP = dO V^T (element i: query 16*(i/8) + 8g +
+  // i%8 of the tile, key `key`); P = exp(scale S - LSE), dS = P (dP - D);
+  // dV^T += dO^T P, dK^T += Q^T dS.  Only the softmax step is inside the
+  // mask branch; the accumulators are updated outside it.
+  auto step = [&](const uint16_t* slot, int qs) {
     const uint16_t* cQ = slot;
     const uint16_t* cG = slot + QT * D;
+    const float* cN = (const float*)(slot + 2 * QT * D);
+    f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
       const int o = row_off<D>(r_off, c);
       s = mfma32(*(const u32x4*)(cQ + o), kreg[c], s);
-      dp = mfma32(*(const u32x4*)(cG + o), vreg[c], dp);
+      dp = mfma32(*(const u32x4*)(cG + o), *(const u32x4*)(sVw + o), dp);
     }
-  };
-  // P = exp(scale S - LSE) and dS = P (dP - D) of the tile starting at
-  // query qs, packed as the B operands of the dV and dK products.  Rows
-  // past Sq have nl = -inf; with a causal mask, query qi sees key `key`
-  // iff key <= qi + off, applied by replacing nl with -inf (no branch).
-  auto pds = [&](const f32x16& s, const f32x16& dp, const uint16_t* slot, int qs, u32x4* pb,
-                 u32x4* dsb) {
-    const float* cN = (const float*)(slot + 2 * QT * D);
-    const int lo = key - off - qs - 8 * g;   // element (c, j) is visible iff 16c + j >= lo
+    // The softmax step and the products in two halves of 16 queries, so only
+    // half of P and dS is live at a time.
+    const bool masked = CAUSAL && key0_wave + 31 > qs + off;
+    const int lo = key - off - qs - 8 * g;   // causal: element (c, j) visible iff 16c + j >= lo
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const f32x4 d0 = *(const f32x4*)(cN + 16 * c + 8 * g);
-      const f32x4 d1 = *(const f32x4*)(cN + 16 * c + 8 * g + 4);
-      const f32x4 l0 = *(const f32x4*)(cN + QT + 16 * c + 8 * g);
-      const f32x4 l1 = *(const f32x4*)(cN + QT + 16 * c + 8 * g + 4);
-      float pv[8], dsv[8];
+      u32x4 pb, dsb;
+      auto softmax = [&](auto msk) {
+        const f32x4 d0 = *(const f32x4*)(cN + 16 * c + 8 * g);
+        const f32x4 d1 = *(const f32x4*)(cN + 16 * c + 8 * g + 4);
+        const f32x4 l0 = *(const f32x4*)(cN + QT + 16 * c + 8 * g);
+        const f32x4 l1 = *(const f32x4*)(cN + QT + 16 * c + 8 * g + 4);
+        float pv[8], dsv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = 8 * c + j;
-        float nl = j < 4 ? l0[j] : l1[j - 4];
-        const float dd = j < 4 ? d0[j] : d1[j - 4];
-        if (CAUSAL) nl = (16 * c + j >= lo) ? nl : kNegInf;
-        const float p = fast_exp2(fmaf(s[i], scale_log2, nl));
-        pv[j] = p;
-        dsv[j] = p * (dp[i] - dd);
-      }
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * c + j;
+          const float nl = j < 4 ? l0[j] : l1[j - 4];
+          const float dd = j < 4 ? d0[j] : d1[j - 4];
+          float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+          if constexpr (decltype(msk)::value) p = (16 * c + j >= lo) ? p : 0.f;
+          pv[j] = p;
+          dsv[j] = p * (dp[i] - dd);
+        }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pb[c][j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
-        dsb[c][j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
-      }
-    }
-  };
-  int cur_qt = 0;   // query tile of the next softmax step
-  auto next_qs = [&]() {
-    const int qs = q_start + cur_qt * QT;
-    if (++cur_qt == n_qt) cur_qt = 0;
-    return qs;
-  };
-  // dV^T += dO^T P,  dK^T += Q^T dS  (contracted over the tile's queries).
-  auto dkdv = [&](const uint16_t* slot, const u32x4* pb, const u32x4* dsb) {
-    const uint16_t* cQ = slot;
-    const uint16_t* cG = slot + QT * D;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
+        for (int j = 0; j < 4; ++j) {
+          pb[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+          dsb[j] = pack_bf16x2(dsv[2 * j], dsv[2 * j + 1]);
+        }
+      };
+      if (masked)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvt[db] = mfma32(tr_col8<D>(cG + 16 * c * D, t_off, db), pb[c], dvt[db]);
-        dkt[db] = mfma32(tr_col8<D>(cQ + 16 * c * D, t_off, db), dsb[c], dkt[db]);
+        dvt[db] = mfma32(tr_col8<D>(cG + 16 * c * D, t_off, db), pb, dvt[db]);
+        dkt[db] = mfma32(tr_col8<D>(cQ + 16 * c * D, t_off, db), dsb, dkt[db]);
       }
+    }
   };
 
-  f32x16 s0, dp0, s1, dp1;
-  u32x4 pb0[2], ds0[2], pb1[2], ds1[2];
-
-  wait_vmcnt0();   // K, V rows and tiles 0, 1 have landed
-  lds_barrier();
-  issue(sT2);
-  sdp(sT0, s0, dp0);
-  pds(s0, dp0, sT0, next_qs(), pb0, ds0);
-  sdp(sT1, s1, dp1);   // unused when there is one tile
-
-  // Body i: tiles i-1 (products), i (softmax), i+1 (S, dP) in slots tPr,
-  // tCu, tNx; the transfer of tile i+2 goes to slot tNw.
-  auto body = [&](const uint16_t* tPr, const uint16_t* tCu, const uint16_t* tNx, uint16_t* tNw,
-                  const f32x16& sCu, const f32x16& dpCu, f32x16& sNx, f32x16& dpNx,
-                  const u32x4* pbPr, const u32x4* dsPr, u32x4* pbCu, u32x4* dsCu) {
-    wait_vmcnt0();   // this wave's part of tile i+1 has landed
-    lds_barrier();   // ... and every wave's; nobody reads tile i-2 any more
-    issue(tNw);
-    const int qs = next_qs();
-    dkdv(tPr, pbPr, dsPr);
-    sdp(tNx, sNx, dpNx);   // past the last tile this reads a stale slot and is unused
-    pds(sCu, dpCu, tCu, qs, pbCu, dsCu);
-    // Issue order: LDS reads a few products ahead; each product followed
-    // by the reads of a later one and a share of the softmax step.
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int k = 0; k < 4 * NDB; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < 2 * NDC; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-    // P(i), dS(i) are computed here, not next to their use in body i+1 (one
-    // statement: each asm statement ends a scheduling region).
-    asm volatile("" ::"v"(pbCu[0]), "v"(pbCu[1]), "v"(dsCu[0]), "v"(dsCu[1]));
+  int cur_qt = 0;   // query tile of the next step
+  auto body = [&](const uint16_t* cur, uint16_t* nxt) {
+    wait_vmcnt0();   // this wave's part of the current tile (and V) has landed
+    lds_barrier();   // ... and every wave's; the other slot is no longer read
+    issue(nxt);
+    const int qs = q_start + cur_qt * QT;
+    if (++cur_qt == n_qt) cur_qt = 0;
+    // Tiles whose queries all precede this wave's first visible key: skip.
+    if (CAUSAL && qs + QT - 1 + off < key0_wave) return;
+    step(cur, qs);
   };
-  int i = 1;
 #pragma clang loop unroll(disable)
-  for (; i + 4 <= n_it; i += 4) {
-    body(sT0, sT1, sT2, sT3, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
-    body(sT1, sT2, sT3, sT0, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
-    body(sT2, sT3, sT0, sT1, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
-    body(sT3, sT0, sT1, sT2, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
-  }
-  if (i < n_it) {
-    body(sT0, sT1, sT2, sT3, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
-    if (++i < n_it) {
-      body(sT1, sT2, sT3, sT0, s0, dp0, s1, dp1, pb1, ds1, pb0, ds0);
-      if (++i < n_it) {
-        body(sT2, sT3, sT0, sT1, s1, dp1, s0, dp0, pb0, ds0, pb1, ds1);
-        ++i;
-      }
-    }
-  }
-  // The products of tile n_it-1 (slot (n_it-1) % 4, register set
-  // (n_it-1) % 2) remain; its data landed before body n_it-2 read it.
-  switch ((n_it - 1) & 3) {
-    case 0: dkdv(sT0, pb0, ds0); break;
-    case 1: dkdv(sT1, pb1, ds1); break;
-    case 2: dkdv(sT2, pb0, ds0); break;
-    default: dkdv(sT3, pb1, ds1); break;
+  for (int i = 0; i < n_it; i += 2) {
+    body(sT0, sT1);
+    if (i + 1 < n_it) body(sT1, sT0);
   }
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;

@@ -233,7 +233,7 @@ __device__ __forceinline__ void row_read_offsets(int n, int g, int* off) {
   const int r = swap23(n);
   const int h = tile_swz<D>(r);
 #pragma unroll
-  for (int c = 0; c < kRowOffs<D>; ++c) off[c] = r * D + 8 * ((2 * c + g) ^ h);
+  for (int c = 0; c < kRowOffs<D>; ++c) off[c] = (r * D + 8 * ((2 * c + g) ^ h)) & 0x3fff;
 }
 template <int D>
 __device__ __forceinline__ int row_off(const int* off, int c) {
@@ -250,7 +250,8 @@ __device__ __forceinline__ void tr_read_offsets(int lane, int* off) {
   const int h = tile_swz<D>(r);
   const int lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
 #pragma unroll
-  for (int db = 0; db < kTrOffs<D>; ++db) off[db] = r * D + 8 * ((4 * db + lc) ^ h) + 4 * (lane & 1);
+  for (int db = 0; db < kTrOffs<D>; ++db)
+    off[db] = (r * D + 8 * ((4 * db + lc) ^ h) + 4 * (lane & 1)) & 0x3fff;
 }
 template <int D>
 __device__ __forceinline__ int tr_off(const int* off, int db) {

@@ -146,7 +146,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
  *   q, k, v, o, d_o   inputs (o and lse as returned by attn_fwd)
  *   lse [B, Hq, Sq]   float32 input
  *   dq  [B, Hq, Sq, d], dk, dv [B, Hkv, Skv, d]   outputs, input dtype
- *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned.
+ *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned; that
+ *   size must stay below 4 GiB (else ATTN_ERR_SHAPE).
  * Supported: bf16 with d in {64, 128}.
  */
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
