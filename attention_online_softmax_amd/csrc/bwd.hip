@@ -264,8 +264,8 @@ struct BwdTile {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, query head, 128-query tile), 32 queries per wave
-// with their Q and dO rows in registers.  Key tiles of 64 rows (K and V)
-// stream through LDS.  Scores are formed transposed, S^T = K Q^T, so each
+// with their Q and dO rows in registers.  Key tiles (K and V) are
+// double-buffered through LDS by buffer loads.  Scores are formed transposed, S^T = K Q^T, so each
 // lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
 // of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
 // ---------------------------------------------------------------------------
@@ -302,8 +302,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  dma_tile<D, BC, 4>(Kh, sK0, 0, Skv, wave, lane);
-  dma_tile<D, BC, 4>(Vh, sV0, 0, Skv, wave, lane);
+  // K/V tiles through buffer loads; rows past Skv arrive as zeros (masked).
+  TileDma<D, BC, 4> dma;
+  dma.init(wave, lane);
+  dma.load(Kh, Skv, sK0, 0, wave);
+  dma.load(Vh, Skv, sV0, 0, wave);
 
   const int qrow = min(row, Sq - 1);
   const uint16_t* Qr = Q + ((int64_t)bh * Sq + qrow) * D;
@@ -330,11 +333,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV, int tt) {
     const int k0 = tt * BC;
-    wait_vmcnt0();
-    __syncthreads();
+    wait_vmcnt0();   // this wave's part of tile tt has landed
+    lds_barrier();   // ... and every wave's; the other buffers are free
     if (tt + 1 < n_tiles) {
-      dma_tile<D, BC, 4>(Kh, nK, k0 + BC, Skv, wave, lane);
-      dma_tile<D, BC, 4>(Vh, nV, k0 + BC, Skv, wave, lane);
+      dma.load(Kh, Skv, nK, k0 + BC, wave);
+      dma.load(Vh, Skv, nV, k0 + BC, wave);
     }
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
@@ -352,24 +355,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         s = mfma32(*(const u32x4*)(kbp + o), qreg[c], s);
         dp = mfma32(*(const u32x4*)(vbp + o), greg[c], dp);
       }
+      // dS^T = P^T (dP^T - D); only this step is inside the mask branch.
       u32x4 dsb[2];
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float dsv[2];
+          for (int j = 0; j < 4; ++j) {
+            float dsv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 8 * c + 2 * j + u;
-            float p = fast_exp2(fmaf(s[i], scale_log2, nl));
-            if (need_mask) {
-              const int kk = ks + 16 * c + 8 * g + 2 * j + u;
-              p = (kk < row_limit) ? p : 0.f;
+            for (int u = 0; u < 2; ++u) {
+              const int i = 8 * c + 2 * j + u;
+              float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+              if constexpr (decltype(masked)::value) {
+                const int kk = ks + 16 * c + 8 * g + 2 * j + u;
+                p = (kk < row_limit) ? p : 0.f;
+              }
+              dsv[u] = p * (dp[i] - dd);
             }
-            dsv[u] = p * (dp[i] - dd);
+            dsb[c][j] = pack_bf16x2(dsv[0], dsv[1]);
           }
-          dsb[c][j] = pack_bf16x2(dsv[0], dsv[1]);
-        }
+      };
+      if (need_mask)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
