@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 // bf16 path: 32x32x16 bf16 MFMA with fp32 accumulation.
 //
-// Four waves per workgroup, 32 query rows per wave.  Scores are formed
+// Four (d64, d128) or eight (d256) waves per workgroup, 32 query rows per
+// wave; the waves share every K/V tile.  Scores are formed
 // transposed, S^T = K Q^T (A = key rows from LDS, B = the wave's queries held
 // in registers), so each lane owns ONE query column and 16 of its scores per
 // 32-key block: the row maximum and row sum are lane-local plus one half-wave
@@ -143,12 +144,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.f;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, int n_qtiles) {
-  constexpr int BR = 128;
+  constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
   constexpr int BC = 32;         // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
-  TileDma<D, BC, 4> dma;
+  TileDma<D, BC, NW> dma;
   dma.init(wave, lane);
 
   const int last_row = min(q0 + BR, Sq) - 1;
@@ -349,14 +350,21 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+// Waves per workgroup: every wave holds 32 query rows, and all waves of a
+// workgroup share each K/V tile, so more waves cut the LDS fills (L2 reads)
+// per FLOP; d256 uses 8 (its 250 registers allow two waves per SIMD, one
+// such workgroup per CU), d64/d128 use 4 (two or three workgroups per CU).
+template <int D>
+constexpr int kFwdWaves = D >= 256 ? 8 : 4;
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-  const int n_qtiles = (a.Sq + 127) / 128;
+  constexpr int NW = kFwdWaves<D>;
+  const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0,
-                     a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3(n_qtiles * BH), dim3(64 * NW), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e,
                      n_qtiles);
   timing_mark(a.stream, 1);
