@@ -136,13 +136,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // transpose reads are free of bank conflicts.
 //
 // Normalisation reference: the exponentials are taken relative to a per-row
-// reference m_ref that only advances when the row maximum exceeds it by more
-// than kLazy (log2 units); o and l are rescaled only then.  o, l and m_ref
-// always describe the same partial softmax (o and l relative to exp2(m_ref)),
-// so O = o / l and LSE = m_ref + log2 l are unchanged in exact arithmetic,
-// and probabilities stay below 2^kLazy.
+// reference m_ref that only advances when a tile's probabilities against it
+// would reach 2^kLazy (detected from their sum, so the common tile needs no
+// row maximum); o and l are rescaled only then.  o, l and m_ref always
+// describe the same partial softmax (o and l relative to exp2(m_ref)), so
+// O = o / l and LSE = m_ref + log2 l are unchanged in exact arithmetic, and
+// probabilities stay below 2^kLazy.
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 8.f;
+constexpr float kLazyBound = 256.f;   // 2^kLazy
 
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
@@ -246,31 +248,44 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   // lpart and pack them as the B operand of the PV product.  Returns the
   // factor by which o must be rescaled (1 unless the reference moved).
   auto softmax = [&](const f32x16* s, u32x4 (*pb)[2]) {
-    float rmax = kNegInf;
+    // Fast path: exponentials against the current reference.  A lane's sum
+    // below 2^kLazy bounds each of its probabilities by 2^kLazy, the same
+    // bound the lazy reference keeps, so no row maximum is needed.  A larger
+    // sum, inf or NaN (e.g. m_ref still -inf on the first tile) takes the
+    // slow path: advance the reference to the row maximum, rescale, redo.
+    auto exps = [&](float msub) {
+      float sum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[kb][i]);
-    const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
-    const bool up = mnew > m_ref + kLazy;
-    const float alpha = up ? fast_exp2(m_ref - mnew) : 1.f;
-    m_ref = up ? mnew : m_ref;
-    const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
-    float lsum = 0.f;
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2, -msub));
+            const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2, -msub));
+            sum += p0 + p1;
+            pb[kb][c][j] = pack_bf16x2(p0, p1);
+          }
+      return sum;
+    };
+    float lsum = exps(m_ref);
+    float alpha = 1.f;
+    if (__any(!(lsum < kLazyBound))) {
+      float rmax = kNegInf;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2, -msub));
-          const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2, -msub));
-          lsum += p0 + p1;
-          pb[kb][c][j] = pack_bf16x2(p0, p1);
-        }
+        for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[kb][i]);
+      const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
+      alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
+      m_ref = mnew;
+      lsum = exps((m_ref == kNegInf) ? 0.f : m_ref);
+    }
     lpart = fmaf(lpart, alpha, lsum);
     return alpha;
   };
+
+
   // O^T += V(tile)^T P^T.
   auto pv = [&](const uint16_t* cV, const u32x4 (*pb)[2]) {
 #pragma unroll
