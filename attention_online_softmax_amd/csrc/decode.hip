@@ -347,8 +347,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel on the matrix cores.  A work unit is one key chunk
-// (split) of one key/value head for up to 8 of its query heads.  The query
+// bf16 split kernel on the matrix cores.  A work unit is one split (every
+// n_splits-th 32-key tile) of one key/value head for up to 8 of its query
+// heads.  The query
 // heads take the place of the query rows of the forward kernel (32 MFMA
 // columns; the ones past the group's heads are fed zeros): per tile of 32
 // keys, S^T = K Q^T (lane = head, 16 scores per lane), the running
@@ -390,9 +391,15 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
   float* ws_l = ws + (int64_t)n_splits * BHq;
   float* ws_acc = ws + 2 * (int64_t)n_splits * BHq;
 
+  // A split takes every n_splits-th 32-key tile of the head's keys (tiles
+  // split, split + n_splits, ...): the waves working on the splits of one
+  // head then stream one contiguous window of K and V together, which the
+  // memory system serves faster than as many separate streams.  Any
+  // partition of the keys gives the same merged result.
+  const int tiles_total = (Skv + TK - 1) / TK;
   struct Unit {
-    int split, hk, hc, b, k0, L;  // keys [k0, k0 + L) of key/value head (b, hk)
-    int rot;                      // tile t of the unit is its tile (t + rot) % n_tiles
+    int split, hk, hc, b;
+    int L;   // tiles of this split
   };
   auto unit_of = [&](int u) {
     Unit x;
@@ -402,25 +409,16 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     r /= n_hchunks;
     x.hk = r % Hkv;
     x.b = r / Hkv;
-    x.k0 = min(x.split * chunk, Skv);
-    x.L = min(x.k0 + chunk, Skv) - x.k0;
-    // Concurrent waves start at different tiles of their chunks, so that they
-    // do not all read the same offsets of equally strided chunks at once.
-    const int nt = (x.L + TK - 1) / TK;
-    x.rot = nt > 0 ? (u / n_splits + x.split) % nt : 0;
+    x.L = x.split < tiles_total ? (tiles_total - x.split + n_splits - 1) / n_splits : 0;
     return x;
   };
-  auto n_tiles = [&](const Unit& x) { return (x.L + TK - 1) / TK; };
-  auto tile_of = [&](const Unit& x, int t) {
-    const int nt = n_tiles(x);
-    const int tt = t + x.rot;
-    return tt >= nt ? tt - nt : tt;
-  };
+  auto n_tiles = [&](const Unit& x) { return x.L; };
+  auto tile_of = [&](const Unit& x, int t) { return x.split + t * n_splits; };
   auto issue = [&](const Unit& x, int t, uint16_t* dK, uint16_t* dV) {
     const int64_t base = (int64_t)(x.b * Hkv + x.hk) * Skv * D;
-    const int r0 = x.k0 + tile_of(x, t) * TK;
-    dma_tile<D, TK, 1>(K + base, dK, r0, x.k0 + x.L, 0, lane);
-    dma_tile<D, TK, 1>(V + base, dV, r0, x.k0 + x.L, 0, lane);
+    const int r0 = tile_of(x, t) * TK;
+    dma_tile<D, TK, 1>(K + base, dK, r0, Skv, 0, lane);
+    dma_tile<D, TK, 1>(V + base, dV, r0, Skv, 0, lane);
   };
   // Raw query rows of the unit's heads (lanes past the group's heads load a
   // valid row and are zeroed by q_keep when the rows are adopted, so that
@@ -532,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
       s = mfma32(*(const u32x4*)(cK + row_off<D>(r_off, c)), qreg[c] ^ qsign, s);
-    const int kvalid = cur.L - tile_of(cur, t) * TK;  // keys of this tile that exist
+    const int kvalid = Skv - tile_of(cur, t) * TK;  // keys of this tile that exist
     float rmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
