@@ -23,9 +23,9 @@ namespace attn {
 
 // ---------------------------------------------------------------------------
 // Per query row: D_i = sum_c dO[i, c] * O[i, c] and nl_i = -LSE_i * log2(e),
-// both fp32, written to the workspace as [D (rows)] [nl (rows)] with each
-// head's rows padded to Sqp = Sq rounded up to 32; padding rows get D = 0
-// and nl = -inf, so their probabilities are exactly 0.
+// both fp32, written to the workspace as pairs (D_i, nl_i) with each head's
+// rows padded to Sqp = Sq rounded up to 32; padding rows get D = 0 and
+// nl = -inf, so their probabilities are exactly 0.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __restrict__ O,
@@ -53,10 +53,8 @@ __global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __res
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
-  if (prow < rows_pad && sub == 0) {
-    ws[prow] = acc;
-    ws[rows_pad + prow] = real ? -LSE[row] * kLog2e : kNegInf;
-  }
+  if (prow < rows_pad && sub == 0)
+    *(f32x2*)(ws + 2 * prow) = f32x2{acc, real ? -LSE[row] * kLog2e : kNegInf};
 }
 
 // Transposed accumulator X^T[d][row] (lane = row n, 16 d values per 32-d
@@ -137,10 +135,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   }
   TileDma<D, QT, 4> dma;
   dma.init(wave, lane);
-  // D and nl of a tile: one float per lane of wave 0 (lanes 0..31 D,
-  // 32..63 nl) through a descriptor over the whole workspace (< 4 GiB).
+  // The (D, nl) pairs of a tile's 32 rows: 256 contiguous bytes, one float
+  // per lane of wave 0, through a descriptor over the whole workspace
+  // (< 4 GiB).
   const rsrc_t ws_rs = make_rsrc(ws, (uint32_t)(2 * rows_pad * 4));
-  const uint32_t dn_lane = ((g ? (uint32_t)rows_pad : 0u) + n) * 4;
   // Transfer of the next iteration tile (query head dma_hh, query tile
   // dma_qt) into `slot`; past the last tile nothing is fetched.
   int dma_hh = 0, dma_qt = 0;
@@ -148,12 +146,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     if (dma_hh >= G) return;
     const int q0 = q_start + dma_qt * QT;
     const int64_t bh = (int64_t)b * Hq + hk * G + dma_hh;
-    dma.load(Q + bh * Sq * D, Sq, slot, q0, wave);
-    dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, wave);
     if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ws_rs, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, (int)dn_lane,
-          (int)((uint32_t)(bh * Sqp + q0) * 4), 0, 0);
+          ws_rs, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, lane * 4,
+          (int)((uint32_t)(bh * Sqp + q0) * 8), 0, 0);
+    dma.load(Q + bh * Sq * D, Sq, slot, q0, wave);
+    dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, wave);
     if (++dma_qt == n_qt) {
       dma_qt = 0;
       ++dma_hh;
@@ -202,16 +200,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     for (int c = 0; c < 2; ++c) {
       u32x4 pb, dsb;
       auto softmax = [&](auto msk) {
-        const f32x4 d0 = *(const f32x4*)(cN + 16 * c + 8 * g);
-        const f32x4 d1 = *(const f32x4*)(cN + 16 * c + 8 * g + 4);
-        const f32x4 l0 = *(const f32x4*)(cN + QT + 16 * c + 8 * g);
-        const f32x4 l1 = *(const f32x4*)(cN + QT + 16 * c + 8 * g + 4);
+        // (D, nl) of queries 16c + 8g + 0..7
+        f32x4 dn[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dn[k] = *(const f32x4*)(cN + 2 * (16 * c + 8 * g) + 4 * k);
         float pv[8], dsv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * c + j;
-          const float nl = j < 4 ? l0[j] : l1[j - 4];
-          const float dd = j < 4 ? d0[j] : d1[j - 4];
+          const float dd = dn[j >> 1][2 * (j & 1)];
+          const float nl = dn[j >> 1][2 * (j & 1) + 1];
           float p = fast_exp2(fmaf(s[i], scale_log2, nl));
           if constexpr (decltype(msk)::value) p = (16 * c + j >= lo) ? p : 0.f;
           pv[j] = p;
@@ -317,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     qreg[c] = *(const u32x4*)(Qr + c * 16 + 8 * g);
     greg[c] = *(const u32x4*)(dOr + c * 16 + 8 * g);
   }
-  const float dd = ws[(int64_t)bh * Sqp + qrow];
-  const float nl = ws[rows_pad + (int64_t)bh * Sqp + qrow];
+  const f32x2 dnl = *(const f32x2*)(ws + 2 * ((int64_t)bh * Sqp + qrow));
+  const float dd = dnl[0], nl = dnl[1];
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

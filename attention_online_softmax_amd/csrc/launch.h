@@ -45,7 +45,7 @@ struct BwdArgs {
   void* dv;
   int B, Hq, Hkv, Sq, Skv, d, causal;
   float scale;
-  float* ws;  // [B, Hq, Sqp] D = rowsum(dO * O), then [B, Hq, Sqp] -LSE * log2(e); Sqp = Sq rounded up to 32
+  float* ws;  // [B, Hq, Sqp] pairs (D = rowsum(dO * O), -LSE * log2(e)); Sqp = Sq rounded up to 32
   hipStream_t stream;
 };
 
