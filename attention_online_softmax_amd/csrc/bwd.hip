@@ -237,6 +237,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   auto body = [&](const uint16_t* cur, uint16_t* nxt) {
     wait_vmcnt0();   // this wave's part of the current tile (and V) has landed
     lds_barrier();   // ... and every wave's; the other slot is no longer read
+    opaque_offsets<kRowOffs<D>>(r_off);
+    opaque_offsets<kTrOffs<D>>(t_off);
     issue(nxt);
     const int qs = q_start + cur_qt * QT;
     if (++cur_qt == n_qt) cur_qt = 0;

@@ -269,6 +269,17 @@ __device__ __forceinline__ u32x4 tr_col8(const uint16_t* rows, const int* off, i
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// An empty statement that the compiler must assume rewrites the N per-lane
+// offsets in place.  At the top of a loop body it keeps the sums LDS base +
+// offset inside the body, where the constant base folds into the immediate
+// offset of the LDS read; otherwise they are hoisted out of the loop and each
+// (base, offset) pair holds a register for the whole loop.
+template <int N>
+__device__ __forceinline__ void opaque_offsets(int* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
