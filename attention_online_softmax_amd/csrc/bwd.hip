@@ -335,6 +335,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int k0 = tt * BC;
     wait_vmcnt0();   // this wave's part of tile tt has landed
     lds_barrier();   // ... and every wave's; the other buffers are free
+    opaque_offsets<kRowOffs<D>>(r_off);
+    opaque_offsets<kTrOffs<D>>(t_off);
     if (tt + 1 < n_tiles) {
       dma.load(Kh, Skv, nK, k0 + BC, wave);
       dma.load(Vh, Skv, nV, k0 + BC, wave);

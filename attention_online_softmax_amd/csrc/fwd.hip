@@ -312,6 +312,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     auto step = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
       wait_vmcnt0();   // this wave's part of tile j has landed
       lds_barrier();   // ... and every wave's; tile j-1 is no longer read
+      opaque_offsets<kRowOffs<D>>(k_off);
+      opaque_offsets<kTrOffs<D>>(v_off);
       dma.load(Kh, Skv, nK, (j + 1) * BC, wave);
       dma.load(Vh, Skv, nV, (j + 1) * BC, wave);
       if (j * BC > wave_kv_last) return;
