@@ -604,6 +604,53 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   const float* ws_m = ws;
   const float* ws_l = ws + (int64_t)n_splits * BHq;
   const float* ws_acc = ws + 2 * (int64_t)n_splits * BHq;
+  T* o = O + (int64_t)bh * D + lane * CPL;
+  if (n_splits <= 16) {
+    // Up to 16 splits: every load of the query head is issued before any
+    // result is used (one memory round trip).  Lane s < n_splits holds
+    // (m_s, l_s); each lane holds its columns of all the accumulators.
+    const int sl = min(lane, n_splits - 1);
+    const float ms = ws_m[(int64_t)sl * BHq + bh];
+    const float ls = ws_l[(int64_t)sl * BHq + bh];
+    float v[16][CPL];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float* src = ws_acc + ((int64_t)min(j, n_splits - 1) * BHq + bh) * D + lane * CPL;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[j][c] = src[c];
+    }
+    const bool own = lane < n_splits;
+    const float M = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(
+                   __builtin_bit_cast(int, group_reduce<16, true>(own ? ms : kNegInf))));
+    const float w = (own && ms != kNegInf) ? fast_exp2(ms - M) : 0.f;
+    const float l = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(
+                   __builtin_bit_cast(int, group_reduce<16, false>(w * ls))));
+    float a[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) a[c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float wj =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) a[c] = fmaf(wj, v[j][c], a[c]);
+    }
+    const float inv = 1.f / l;
+    if constexpr (CPL == 1) {
+      if constexpr (sizeof(T) == 4) {
+        o[0] = a[0] * inv;
+      } else {
+        o[0] = f32_to_bf16(a[0] * inv);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; c += 2) Elem<T>::store2(o + c, a[c] * inv, a[c + 1] * inv);
+    }
+    if (LSE && lane == 0) LSE[bh] = (M + fast_log2(l)) * kLn2;
+    return;
+  }
   float M = kNegInf;
   for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, ws_m[(int64_t)s * BHq + bh]);
   M = group_reduce<64, true>(M);
@@ -641,7 +688,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   }
   l = group_reduce<64, false>(l);
   const float inv = 1.f / l;
-  T* o = O + (int64_t)bh * D + lane * CPL;
   if constexpr (CPL == 1) {
     if constexpr (sizeof(T) == 4) {
       o[0] = a[0] * inv;
