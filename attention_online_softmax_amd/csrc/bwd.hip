@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
       const int o = row_off<D>(r_off, c);
-      s = mfma32(*(const u32x4*)(cQ + o), kreg[c], s);
-      dp = mfma32(*(const u32x4*)(cG + o), *(const u32x4*)(sVw + o), dp);
+      s = mfma32(lds_row(cQ, o), kreg[c], s);
+      dp = mfma32(lds_row(cG, o), lds_row(sVw, o), dp);
     }
     // The softmax step and the products in two halves of 16 queries, so only
     // half of P and dS is live at a time.
@@ -354,8 +354,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
         const int o = row_off<D>(r_off, c);
-        s = mfma32(*(const u32x4*)(kbp + o), qreg[c], s);
-        dp = mfma32(*(const u32x4*)(vbp + o), greg[c], dp);
+        s = mfma32(lds_row(kbp, o), qreg[c], s);
+        dp = mfma32(lds_row(vbp, o), greg[c], dp);
       }
       // dS^T = P^T (dP^T - D); only this step is inside the mask branch.
       u32x4 dsb[2];

@@ -217,27 +217,33 @@ struct TileDma {
   }
 };
 
-// Per-lane element offsets into a swizzled [*, D] tile.  The XOR group is 16
+// Per-lane byte offsets into a swizzled [*, D] tile.  The XOR group is 16
 // chunks (128 elements), so D = 256 keeps the offsets of its first 128
-// columns in registers and adds 128 for the rest.
+// columns in registers and adds 256 bytes for the rest.  Byte offsets are
+// added to the tile's address as they are (no shift per read).
 template <int D>
 constexpr int kRowOffs = D >= 256 ? 8 : D / 16;
 template <int D>
 constexpr int kTrOffs = D >= 256 ? 4 : D / 32;
 
+// 16-byte LDS read at byte offset `boff` from the tile at `base`.
+__device__ __forceinline__ u32x4 lds_row(const uint16_t* base, int boff) {
+  return *(const u32x4*)((const char*)base + boff);
+}
+
 // b128 row read that feeds MFMA A-row n of a 32-row block (physical row
 // swap23(n)) with logical chunk 2c + g, i.e. k-step c of a contraction over
-// the D columns (c = 0 .. D/16-1): offset row_off<D>(off, c).
+// the D columns (c = 0 .. D/16-1): lds_row(tile, row_off<D>(off, c)).
 template <int D>
 __device__ __forceinline__ void row_read_offsets(int n, int g, int* off) {
   const int r = swap23(n);
   const int h = tile_swz<D>(r);
 #pragma unroll
-  for (int c = 0; c < kRowOffs<D>; ++c) off[c] = (r * D + 8 * ((2 * c + g) ^ h)) & 0x3fff;
+  for (int c = 0; c < kRowOffs<D>; ++c) off[c] = (2 * (r * D + 8 * ((2 * c + g) ^ h))) & 0x7fff;
 }
 template <int D>
 __device__ __forceinline__ int row_off(const int* off, int c) {
-  return off[c % kRowOffs<D>] + 128 * (c / kRowOffs<D>);
+  return off[c % kRowOffs<D>] + 256 * (c / kRowOffs<D>);
 }
 
 // Transpose reads of 32-column block db (db = 0 .. D/32-1) for rows
@@ -251,11 +257,11 @@ __device__ __forceinline__ void tr_read_offsets(int lane, int* off) {
   const int lc = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
 #pragma unroll
   for (int db = 0; db < kTrOffs<D>; ++db)
-    off[db] = (r * D + 8 * ((4 * db + lc) ^ h) + 4 * (lane & 1)) & 0x3fff;
+    off[db] = (2 * (r * D + 8 * ((4 * db + lc) ^ h) + 4 * (lane & 1))) & 0x7fff;
 }
 template <int D>
 __device__ __forceinline__ int tr_off(const int* off, int db) {
-  return off[db % kTrOffs<D>] + 128 * (db / kTrOffs<D>);
+  return off[db % kTrOffs<D>] + 256 * (db / kTrOffs<D>);
 }
 
 // k-operand of a 32x32x16 MFMA contracted over 8 consecutive ROWS of a
@@ -264,8 +270,9 @@ __device__ __forceinline__ int tr_off(const int* off, int db) {
 template <int D>
 __device__ __forceinline__ u32x4 tr_col8(const uint16_t* rows, const int* off, int db) {
   constexpr int X = D >= 128 ? 2 : 1;   // rows + 4: the swizzle's top bit flips
-  const u32x2 a = lds_tr4(rows + tr_off<D>(off, db));
-  const u32x2 b = lds_tr4(rows + tr_off<D>(off, db ^ X) + 4 * D);
+  const char* base = (const char*)rows;
+  const u32x2 a = lds_tr4((const uint16_t*)(base + tr_off<D>(off, db)));
+  const u32x2 b = lds_tr4((const uint16_t*)(base + tr_off<D>(off, db ^ X) + 8 * D));
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 

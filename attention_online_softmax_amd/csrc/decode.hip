@@ -529,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
-      s = mfma32(*(const u32x4*)(cK + row_off<D>(r_off, c)), qreg[c] ^ qsign, s);
+      s = mfma32(lds_row(cK, row_off<D>(r_off, c)), qreg[c] ^ qsign, s);
     const int kvalid = Skv - tile_of(cur, t) * TK;  // keys of this tile that exist
     float rmax = kNegInf;
 #pragma unroll

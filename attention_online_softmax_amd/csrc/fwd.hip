@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [0, row_limit)
 
-  // Per-lane LDS offsets (elements) into the swizzled tiles.
+  // Per-lane LDS byte offsets into the swizzled tiles.
   int k_off[kRowOffs<D>], v_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, k_off);
   tr_read_offsets<D>(lane, v_off);
@@ -229,8 +229,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma32(*(const u32x4*)(cK + kb * 32 * D + row_off<D>(k_off, c)),
-                       qreg[c], s[kb]);
+        s[kb] = mfma32(lds_row(cK + kb * 32 * D, row_off<D>(k_off, c)), qreg[c], s[kb]);
+    // Keep three K reads in flight ahead of the products; left alone, the
+    // scheduler issues each read right before its product at this register
+    // pressure and every product waits for the LDS latency.
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // 3 LDS reads
+#pragma unroll
+    for (int i = 0; i < NDC * NKB - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   };
   // Scores of keys at or beyond the row's limit become -inf.
   auto mask = [&](f32x16* s, int k0) {
