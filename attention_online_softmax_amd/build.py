@@ -39,10 +39,19 @@ def device_flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file extra flags.  The backward kernels run about 2 % faster under
+# LLVM's iterative ILP scheduling strategy; the forward and decode kernels
+# are fastest with the default one.
+FILE_FLAGS = {
+    "bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + device_flags() + lang + ["-c", src, "-o", obj]
+    cmd = ([hipcc()] + device_flags() + FILE_FLAGS.get(os.path.basename(src), []) + lang +
+           ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in line)
