@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kAbiVersion = 1;
 constexpr int kMaxSplits = 256;
-constexpr int kDecodeMaxChunk = 1024;
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi)
@@ -143,7 +142,6 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
   if (!decode_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_VALUE;
-  if ((Skv + n_splits - 1) / n_splits > kDecodeMaxChunk) return ATTN_ERR_VALUE;
   if (!workspace) return ATTN_ERR_WORKSPACE;
   if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, d, n_splits)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||

@@ -114,14 +114,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int n_splits);
  *   workspace >= attn_decode_workspace_bytes(B, Hq, d, n_splits) bytes of
  *             device memory, 16-byte aligned; contents on entry are ignored
  *             and on exit unspecified.
- * The keys are cut into n_splits contiguous chunks of ceil(Skv / n_splits)
- * keys (trailing chunks may be short or empty).  A first kernel computes each
- * chunk's unnormalised state (m, l, acc) for all Hq / Hkv query heads of a
- * key/value head in one pass over that chunk's keys and values; a second
- * kernel folds the n_splits states of each query with the monoid merge and
- * writes O = acc / l and lse = m + ln l.  1 <= n_splits <= 256 and
- * ceil(Skv / n_splits) <= 1024 (one chunk's scores live in LDS), else
- * ATTN_ERR_VALUE.
+ * The keys are partitioned into n_splits sets: for bf16 with d in {64, 128},
+ * split s takes the 32-key tiles s, s + n_splits, s + 2 n_splits, ...;
+ * otherwise split s is the contiguous chunk [s c, (s + 1) c) with
+ * c = ceil(Skv / n_splits).  Trailing splits may be empty.  A first kernel
+ * computes each split's unnormalised state (m, l, acc) for all Hq / Hkv
+ * query heads of a key/value head in one pass over that split's keys and
+ * values; a second kernel folds the n_splits states of each query with the
+ * monoid merge and writes O = acc / l and lse = m + ln l.  The merge is
+ * associative and commutative, so every partition gives the same result up
+ * to rounding.  1 <= n_splits <= 256, else ATTN_ERR_VALUE.
  * Supported d: {64, 128, 256} for both dtypes.
  */
 attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,

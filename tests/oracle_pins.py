@@ -311,6 +311,22 @@ def pin_monoid_chunkings(A):
                 Or, Lr = A.online_softmax_recurrence(s, v[0, 0], blk)
                 _close(Or, O[0, h], 1e-13, f"recurrence {blk} O")
                 _close(Lr, L[0, h], 1e-13, f"recurrence {blk} LSE")
+    # Non-contiguous partitions: key tiles of tk keys dealt to n sets (tile t
+    # to set t % n; some sets empty), the sets' states merged in a shuffled
+    # order, give the unchunked result too (associativity and commutativity).
+    for causal in (False, True):
+        O, L = A.attention_ref(q, k, v, causal, scale)
+        for h in range(Hq):
+            s = A.scores(q, k, causal, scale, 0, h)
+            for n, tk in ((3, 4), (5, 2), (16, 2), (7, 1)):
+                sets = [[j for j in range(Skv) if (j // tk) % n == t] for t in range(n)]
+                states = [A.block_state(s[:, idx], v[0, 0][idx]) for idx in sets]
+                st = A.identity_state(Sq, d)
+                for i in rng.permutation(n):
+                    st = A.merge(st, states[i])
+                Om, Lm = A.finalize(st)
+                _close(Om, O[0, h], 1e-13, f"dealt tiles n={n} tk={tk} O")
+                _close(Lm, L[0, h], 1e-13, f"dealt tiles n={n} tk={tk} LSE")
     # commutativity of merge on real states
     s = _rand(28, 4, 10)
     vv = _rand(29, 10, 3)

@@ -121,7 +121,6 @@ def test_decode_validation():
     assert call(d=80) == UNSUP
     assert call(n=0) == VALUE
     assert call(n=257) == VALUE
-    assert call(Skv=1 << 20, n=16) == VALUE          # chunk above the per-workgroup limit
     assert call(ws=None) == WS
     assert call(wsb=need - 1) == WS
     assert call(ws=ws + 8) == ALIGN

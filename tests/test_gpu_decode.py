@@ -13,7 +13,9 @@ pytestmark = pytest.mark.gpu
 
 # (B, Hq, Hkv, Skv, d, n_splits, dtype): grouped heads from 1 to 16 per
 # key/value head (16 uses two head chunks), ragged chunks, empty trailing
-# chunks (n_splits * chunk > Skv), a single key, one split.
+# chunks (n_splits * chunk > Skv), a single key, one split, and splits of
+# more than 1024 keys on every kernel (bf16 d128 on the matrix cores, fp32
+# and bf16 d256 on the vector units).
 CASES = [
     (2, 8, 2, 1000, 128, 16, "bf16"),
     (1, 4, 4, 513, 64, 7, "bf16"),
@@ -21,6 +23,9 @@ CASES = [
     (2, 2, 1, 1, 128, 1, "bf16"),
     (1, 4, 1, 10, 128, 16, "bf16"),
     (1, 8, 1, 1024, 128, 1, "bf16"),
+    (1, 8, 2, 3000, 128, 1, "bf16"),
+    (1, 4, 2, 2100, 256, 1, "bf16"),
+    (2, 4, 1, 2500, 64, 2, "f32"),
     (2, 8, 2, 777, 128, 16, "f32"),
     (1, 3, 1, 200, 64, 3, "f32"),
     (1, 2, 2, 90, 256, 4, "f32"),
