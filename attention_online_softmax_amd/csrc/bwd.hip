@@ -8,10 +8,10 @@
 // With P = exp(scale Q K^T + C - LSE):
 //   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// Three kernels: per query row D and -LSE log2(e); dK and dV per key tile
-// (looping over the query tiles and the query heads of a grouped key/value
-// head, so every dK/dV element is written once); dQ per query tile.  No
-// atomics.  Both product kernels stream their tiles HBM -> LDS with
+// Two kernels: dQ per query tile, which also forms D and -LSE log2(e) per
+// query row and passes them on through the workspace; then dK and dV per key
+// tile (looping over the query tiles and the query heads of a grouped
+// key/value head, so every dK/dV element is written once).  No atomics.  Both product kernels stream their tiles HBM -> LDS with
 // global_load_lds into double-buffered, swizzled tiles (see common.h) that
 // are read both by rows and, through transpose reads, by columns.
 #include <type_traits>
@@ -20,42 +20,6 @@
 #include "launch.h"
 
 namespace attn {
-
-// ---------------------------------------------------------------------------
-// Per query row: D_i = sum_c dO[i, c] * O[i, c] and nl_i = -LSE_i * log2(e),
-// both fp32, written to the workspace as pairs (D_i, nl_i) with each head's
-// rows padded to Sqp = Sq rounded up to 32; padding rows get D = 0 and
-// nl = -inf, so their probabilities are exactly 0.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dot_do_o_kernel(const uint16_t* __restrict__ O,
-                                                           const uint16_t* __restrict__ dO,
-                                                           const float* __restrict__ LSE,
-                                                           float* __restrict__ ws, int Sq, int Sqp,
-                                                           int64_t rows_pad) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const int64_t prow = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // padded row
-  const int sub = threadIdx.x % LPR;
-  const int64_t bh = prow / Sqp;
-  const int q = (int)(prow - bh * Sqp);
-  const bool real = prow < rows_pad && q < Sq;
-  const int64_t row = bh * Sq + q;
-  float acc = 0.f;
-  if (real) {
-    const u32x4 o = *(const u32x4*)(O + row * D + sub * 8);
-    const u32x4 g = *(const u32x4*)(dO + row * D + sub * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(__uint_as_float(o[i] << 16), __uint_as_float(g[i] << 16), acc);
-      acc = fmaf(__uint_as_float(o[i] & 0xffff0000u), __uint_as_float(g[i] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
-  if (prow < rows_pad && sub == 0)
-    *(f32x2*)(ws + 2 * prow) = f32x2{acc, real ? -LSE[row] * kLog2e : kNegInf};
-}
 
 // Transposed accumulator X^T[d][row] (lane = row n, 16 d values per 32-d
 // block) stored to row-major X[row][d] after multiplying by `mul`.
@@ -264,7 +228,12 @@ struct BwdTile {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, query head, 128-query tile), 32 queries per wave
-// with their Q and dO rows in registers.  Key tiles (K and V) are
+// with their Q and dO rows in registers.  It runs first and also forms, per
+// query row, D_i = sum_c dO[i, c] O[i, c] and nl_i = -LSE_i * log2(e),
+// which it uses itself and writes to the workspace as pairs (D_i, nl_i) for
+// the dK/dV kernel; each head's rows are padded to Sqp = Sq rounded up to
+// 32 and the padding rows get (0, -inf), so their probabilities are exactly
+// 0 there.  Key tiles (K and V) are
 // double-buffered through LDS by buffer loads.  Scores are formed transposed, S^T = K Q^T, so each
 // lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
 // of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
@@ -272,9 +241,9 @@ struct BwdTile {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dQ,
-    int BH, int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale, float scale_log2,
-    int n_qtiles, int64_t rows_pad) {
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
+    const float* __restrict__ LSE, float* __restrict__ ws, uint16_t* __restrict__ dQ, int BH,
+    int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale, float scale_log2, int n_qtiles) {
   constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -317,8 +286,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     qreg[c] = *(const u32x4*)(Qr + c * 16 + 8 * g);
     greg[c] = *(const u32x4*)(dOr + c * 16 + 8 * g);
   }
-  const f32x2 dnl = *(const f32x2*)(ws + 2 * ((int64_t)bh * Sqp + qrow));
-  const float dd = dnl[0], nl = dnl[1];
+  // D over this lane's half of the columns, plus the other half (lane ^ 32).
+  const uint16_t* Or = O + ((int64_t)bh * Sq + qrow) * D;
+  float dacc = 0.f;
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    const u32x4 ov = *(const u32x4*)(Or + c * 16 + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dacc = fmaf(__uint_as_float(ov[i] << 16), __uint_as_float(greg[c][i] << 16), dacc);
+      dacc = fmaf(__uint_as_float(ov[i] & 0xffff0000u), __uint_as_float(greg[c][i] & 0xffff0000u),
+                  dacc);
+    }
+  }
+  dacc = halfwave_sum(dacc);
+  const float dd = valid ? dacc : 0.f;
+  const float nl = valid ? -LSE[(int64_t)bh * Sq + qrow] * kLog2e : kNegInf;
+  if (g == 0 && row < Sqp) *(f32x2*)(ws + 2 * ((int64_t)bh * Sqp + row)) = f32x2{dd, nl};
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -403,15 +387,18 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int Sqp = (a.Sq + 31) / 32 * 32;
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
-  constexpr int RPB = 256 / (D / 8);
+  const float sl2 = a.scale * kLog2e;
+  // dQ first: it also writes the (D, nl) pairs the dK/dV kernel reads.
+  const int n_qtiles = (a.Sq + 127) / 128;
+  const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_dot_do_o_kernel<D>), dim3((rows_pad + RPB - 1) / RPB), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, a.Sq,
-                     Sqp, rows_pad);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
+                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.scale, sl2, n_qtiles);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const float sl2 = a.scale * kLog2e;
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
   timing_mark(a.stream, 2);
@@ -420,16 +407,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
                      BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.scale, sl2, rows_pad);
   timing_mark(a.stream, 3);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qtiles = (a.Sq + 127) / 128;
-  const int BH = a.B * a.Hq;
-  timing_mark(a.stream, 4);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dq, BH, a.Hq, a.Hkv,
-                     a.Sq, Sqp, a.Skv, a.scale, sl2, n_qtiles, rows_pad);
-  timing_mark(a.stream, 5);
   return hipGetLastError();
 }
 

@@ -38,10 +38,10 @@ METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak; decode HBM GB/s + % peak
 # (the i-th kernel of each call, matching the timing-event slots).
 KERNELS = {
     "fwd": ["fwd_bf16_kernel"],
-    "bwd": ["bwd_dot_do_o_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+    "bwd": ["bwd_dq_kernel", "bwd_dkdv_kernel"],
     "decode": ["decode_split_kernel", "decode_combine_kernel"],
 }
-SOURCES = {"fwd_bf16_kernel": "fwd.hip", "bwd_dot_do_o_kernel": "bwd.hip",
+SOURCES = {"fwd_bf16_kernel": "fwd.hip",
            "bwd_dkdv_kernel": "bwd.hip", "bwd_dq_kernel": "bwd.hip",
            "decode_split_kernel": "decode.hip", "decode_combine_kernel": "decode.hip"}
 
@@ -93,16 +93,14 @@ def per_kernel_algorithmic(w):
     es = 2
     q_bytes = w.B * w.Hq * w.Sq * w.d * es
     kv_bytes = w.B * w.Hkv * w.Skv * w.d * es
-    lse_bytes = w.B * w.Hq * w.Sq * 4
     out = {
         # forward: Q K^T and P V, 2 FLOP per multiply-add each
         "fwd_bf16_kernel": ("mfma", 4.0 * w.d * pairs),
-        # D = rowsum(dO * O): read O and dO, write D
-        "bwd_dot_do_o_kernel": ("hbm", 2.0 * q_bytes + lse_bytes),
         # S, dP, dV and dK products (the recomputed S is one of the five
         # backward products, so it is credited here)
         "bwd_dkdv_kernel": ("mfma", 8.0 * w.d * pairs),
-        # dQ product only; its recomputation of S and dP is not credited
+        # dQ product only; its recomputation of S and dP, and its D = rowsum(dO * O)
+        # per query row, are not credited
         "bwd_dq_kernel": ("mfma", 2.0 * w.d * pairs),
     }
     if w.kind == "decode":
@@ -280,7 +278,7 @@ def bench_fwd_bwd(args, hev, stream):
                      dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["ws"])
 
     calls = [("fwd", fwd), ("bwd", bwd)]
-    nk = {"fwd": 1, "bwd": 3}
+    nk = {"fwd": 1, "bwd": 2}
     for i in range(args.warmup):
         fwd(i)
         bwd(i)

@@ -165,8 +165,8 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
  * point records events[2i] on its stream just before the i-th kernel it
  * launches and events[2i+1] just after it, for 2i+1 < n; the caller reads
  * the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
- * (the forward kernel), attn_decode 2 (split, combine), attn_bwd 3
- * (D = rowsum(dO*O), dK/dV, dQ).  Pass NULL or n = 0 to stop.  The library
+ * (the forward kernel), attn_decode 2 (split, combine), attn_bwd 2
+ * (dQ together with D = rowsum(dO*O), then dK/dV).  Pass NULL or n = 0 to stop.  The library
  * neither creates nor destroys the events.  Returns ATTN_ERR_VALUE if n < 0.
  */
 attn_status attn_set_timing_events(void* const* events, int n);
