@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     attention_ref,
     block_state,
     decode_combine,
+    decode_paged_ref,
     decode_partials,
     decode_ref,
     finalize,
@@ -18,6 +19,7 @@ from .attention import (  # noqa: F401
     mask_matrix,
     merge,
     online_softmax_recurrence,
+    paged_gather,
     scores,
     split_bounds,
 )

@@ -34,6 +34,11 @@ Readings where the pages are silent (each is also listed in the design notes):
   exp(-inf - -inf);
 * split-KV boundaries are contiguous chunks of ceil(Skv / n_splits) keys, the
   last one possibly shorter (or empty), partials left unnormalised;
+* paged decode: the key/value pools are [n_pages, Hkv, page_size, d]; key t
+  of stream b is row t % page_size of page block_table[b, t // page_size];
+  the stream's length is clamped to [0, max_pages * page_size]; a page id
+  outside [0, n_pages) stands for a page of zeros; a stream with no keys
+  has O = 0 and LSE = -inf (the definition needs at least one allowed key);
 * the backward is the plain derivative of the definition, with P recomputed
   from the saved LSE: dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij,
   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q, grouped heads summing
@@ -321,6 +326,50 @@ def decode_combine(m, l, acc):
 def decode_ref(q, k, v, scale, n_splits):
     """Split-KV decode: partial states per chunk, combined by the monoid."""
     return decode_combine(*decode_partials(q, k, v, scale, n_splits))
+
+
+# ---------------------------------------------------------------------------
+# Paged, variable-length decode.  Paging changes only where the keys are
+# stored: the result is attention of each stream's query row over that
+# stream's keys in order ("Compilers and Kernels", FlashAttention section,
+# first display equation), with all of its keys visible.
+# ---------------------------------------------------------------------------
+
+def paged_gather(pages, block_table, b, seq_len):
+    """Keys (or values) 0 .. L-1 of stream b as a contiguous [Hkv, L, d]
+    array.  pages: [n_pages, Hkv, page_size, d]; block_table: [B, max_pages]
+    integers; L = seq_len clamped to [0, max_pages * page_size].  Key t is
+    row t % page_size of page block_table[b, t // page_size]; a page id
+    outside [0, n_pages) stands for a page of zeros."""
+    n_pages, Hkv, ps, d = pages.shape
+    L = min(max(int(seq_len), 0), block_table.shape[1] * ps)
+    t = np.arange(L)
+    pid = np.asarray(block_table[b])[t // ps].astype(np.int64)
+    ok = (pid >= 0) & (pid < n_pages)
+    out = np.zeros((L, Hkv, d))
+    out[ok] = pages[pid[ok], :, (t % ps)[ok], :]
+    return out.transpose(1, 0, 2)
+
+
+def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, scale):
+    """Paged decode.  q: [B, Hq, 1, d]; k_pages, v_pages: [n_pages, Hkv,
+    page_size, d]; block_table: [B, max_pages]; seq_lens: [B].  Returns
+    O [B, Hq, 1, dv] and LSE [B, Hq, 1]; a stream with no keys gets O = 0
+    and LSE = -inf."""
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query row per head")
+    dv = v_pages.shape[-1]
+    O = np.zeros((B, Hq, 1, dv))
+    LSE = np.full((B, Hq, 1), NEG_INF)
+    for b in range(B):
+        kb = paged_gather(k_pages, block_table, b, seq_lens[b])
+        if kb.shape[1] == 0:
+            continue
+        vb = paged_gather(v_pages, block_table, b, seq_lens[b])
+        o, lse = attention_ref(q[b:b + 1], kb[None], vb[None], False, scale)
+        O[b], LSE[b] = o[0], lse[0]
+    return O, LSE
 
 
 # ---------------------------------------------------------------------------

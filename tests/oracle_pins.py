@@ -383,6 +383,66 @@ def pin_decode(A):
             _close(m[sp] + np.log(l[sp]), Lc[:, :, 0], 1e-13, "split partial LSE")
 
 
+def pin_decode_paged(A):
+    """Paged decode equals plain attention of each stream's query over its
+    first seq_len keys, written out contiguously: an identity block table,
+    a shuffled page pool, ragged, empty, negative and over-capacity lengths,
+    and page ids outside the pool (pages of zeros)."""
+    B, Hq, Hkv, S, d, ps = 3, 4, 2, 40, 6, 8
+    npg = S // ps
+    k = _rand(60, B, Hkv, S, d)
+    v = _rand(61, B, Hkv, S, d)
+    q = _rand(62, B, Hq, 1, d, mult=2.0)
+    scale = 0.4
+    rng = _rng(63)
+
+    def pool(x):  # page b * npg + i holds rows [i ps, (i + 1) ps) of stream b
+        return x.reshape(B, Hkv, npg, ps, d).transpose(0, 2, 1, 3, 4).reshape(B * npg, Hkv, ps, d)
+
+    def plain(kk, vv, lens):
+        O = np.zeros((B, Hq, 1, d))
+        L = np.full((B, Hq, 1), -math.inf)
+        for b in range(B):
+            n = int(min(max(lens[b], 0), S))
+            if n:
+                O[b:b + 1], L[b:b + 1] = A.attention_ref(q[b:b + 1], kk[b:b + 1, :, :n],
+                                                         vv[b:b + 1, :, :n], False, scale)
+        return O, L
+
+    kp, vp = pool(k), pool(v)
+    table = np.arange(B * npg).reshape(B, npg)
+    for lens in ([S, 17, 1], [8, 9, 33], [0, S + 100, -5]):
+        lens = np.array(lens)
+        O, L = A.decode_paged_ref(q, kp, vp, table, lens, scale)
+        Or, Lr = plain(k, v, lens)
+        _close(O, Or, 1e-14, f"paged O lens={lens.tolist()}")
+        assert np.array_equal(np.isinf(L), np.isinf(Lr)), "empty streams"
+        _close(np.where(np.isinf(L), 0, L), np.where(np.isinf(Lr), 0, Lr), 1e-14, "paged LSE")
+        # the same pages at shuffled places in the pool
+        perm = rng.permutation(B * npg)
+        kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+        kp2[perm], vp2[perm] = kp, vp
+        O2, L2 = A.decode_paged_ref(q, kp2, vp2, perm[table], lens, scale)
+        assert np.array_equal(O2, O) and np.array_equal(L2, L), "shuffled pool"
+    # full lengths: the split-KV decode of the contiguous cache
+    Od, Ld = A.decode_ref(q, k, v, scale, 5)
+    O, L = A.decode_paged_ref(q, kp, vp, table, np.full(B, S), scale)
+    _close(O, Od, 1e-13, "paged vs split decode O")
+    _close(L, Ld, 1e-13, "paged vs split decode LSE")
+    # page ids outside the pool read as zeros
+    bad = table.copy()
+    bad[0, 1], bad[1, 4] = -1, B * npg
+    kz, vz = k.copy(), v.copy()
+    kz[0, :, ps:2 * ps] = 0
+    vz[0, :, ps:2 * ps] = 0
+    kz[1, :, 4 * ps:5 * ps] = 0
+    vz[1, :, 4 * ps:5 * ps] = 0
+    O, L = A.decode_paged_ref(q, kp, vp, bad, np.full(B, S), scale)
+    Or, Lr = plain(kz, vz, np.full(B, S))
+    _close(O, Or, 1e-14, "invalid page ids O")
+    _close(L, Lr, 1e-14, "invalid page ids LSE")
+
+
 # ---------------------------------------------------------------- backward
 
 def _loss_grad_fd(A, q, k, v, do, causal, scale, eps=1e-6):
@@ -496,6 +556,6 @@ def pin_bwd_identities(A):
 FORWARD_PINS = [pin_fwd_mpmath, pin_fwd_golden, pin_fwd_uniform, pin_fwd_onehot,
                 pin_fwd_single_key, pin_fwd_scipy, pin_fwd_torch_sdpa, pin_fwd_invariants]
 MONOID_PINS = [pin_monoid_golden, pin_monoid_identity, pin_monoid_chunkings, pin_monoid_lse]
-DECODE_PINS = [pin_decode]
+DECODE_PINS = [pin_decode, pin_decode_paged]
 BACKWARD_PINS = [pin_bwd_finite_difference, pin_bwd_autograd, pin_bwd_golden, pin_bwd_identities]
 ALL_PINS = FORWARD_PINS + MONOID_PINS + DECODE_PINS + BACKWARD_PINS

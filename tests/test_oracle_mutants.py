@@ -44,6 +44,16 @@ MUTANTS = [
     ("split chunk floor", "c = -(-Skv // n_splits)", "c = max(Skv // n_splits, 1)", 0),
     ("decode without scale", "s = (q[b, h] @ k[b, h // g].T) * scale",
      "s = (q[b, h] @ k[b, h // g].T)", 0),
+    ("paged row within page", "out[ok] = pages[pid[ok], :, (t % ps)[ok], :]",
+     "out[ok] = pages[pid[ok], :, ((t + 1) % ps)[ok], :]", 0),
+    ("paged page of next key", "pid = np.asarray(block_table[b])[t // ps]",
+     "pid = np.asarray(block_table[b])[np.minimum((t + 1) // ps, block_table.shape[1] - 1)]", 0),
+    ("paged length unclamped", "L = min(max(int(seq_len), 0), block_table.shape[1] * ps)",
+     "L = max(int(seq_len), 0)", 0),
+    ("paged invalid id wraps", "ok = (pid >= 0) & (pid < n_pages)",
+     "pid = pid % n_pages\n    ok = pid >= 0", 0),
+    ("paged empty stream NaN", "        if kb.shape[1] == 0:\n            continue",
+     "        if kb.shape[1] == 0:\n            O[b] = np.nan\n            continue", 0),
     ("bwd dS sign", "ds = p * (dp - D[:, None])", "ds = p * (dp + D[:, None])", 0),
     ("bwd dK without scale", "dk[b, h // g] += scale * (ds.T @ q[b, h])",
      "dk[b, h // g] += (ds.T @ q[b, h])", 0),
