@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_bytes,
     attn_decode,
+    attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_set_timing_events,

@@ -23,8 +23,8 @@ STATUS_NAMES = {
     8: "ATTN_ERR_VALUE",
 }
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_set_timing_events")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
+           "attn_bwd_workspace_bytes", "attn_bwd", "attn_set_timing_events")
 
 _lib = None
 
@@ -57,6 +57,9 @@ def lib():
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode.restype = i
     L.attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode_paged.restype = i
+    L.attn_decode_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp,
+                                    sz, vp]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_bwd.restype = i
@@ -172,6 +175,41 @@ def attn_decode(q, k_cache, v_cache, scale=None, n_splits=16, o=None, lse=None,
                            _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_decode")
+    return o, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, n_splits=16,
+                      o=None, lse=None, workspace=None, stream=None):
+    """Paged, variable-length decode.  q [B,Hq,1,d]; pools [n_pages,Hkv,page_size,d];
+    block_table [B,max_pages] and seq_lens [B] int32 on the same GPU; returns (o, lse)."""
+    _check([q, k_pages, v_pages, block_table, seq_lens],
+           ["q", "k_pages", "v_pages", "block_table", "seq_lens"])
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per head: q must be [B, Hq, 1, d]")
+    n_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or tuple(block_table.shape[:1]) != (B,) \
+            or tuple(seq_lens.shape) != (B,):
+        raise ValueError("inconsistent paged-cache shapes")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, 1), device=q.device, dtype=torch.float32)
+    need = attn_decode_workspace_bytes(B, Hq, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    st = lib().attn_decode_paged(_dtype_code(q), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                 _ptr(block_table), _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                 d, n_pages, page_size, max_pages, float(scale), int(n_splits),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_decode_paged")
     return o, lse
 
 

@@ -28,6 +28,7 @@ Span span(const void* p, int64_t bytes) {
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int esize(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
@@ -36,6 +37,7 @@ bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
 bool fwd_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
 bool decode_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
 bool bwd_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
+bool paged_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
 
 // Per-head element counts must stay within 32-bit index arithmetic.
 bool sizes_ok(int64_t S, int d) { return S * (int64_t)d < (int64_t(1) << 31); }
@@ -99,6 +101,7 @@ int attn_supports(int dtype, int entry, int d) {
     case 0: return fwd_d_ok(dtype, d);
     case 1: return decode_d_ok(dtype, d);
     case 2: return bwd_d_ok(dtype, d);
+    case 3: return paged_d_ok(dtype, d);
   }
   return 0;
 }
@@ -158,6 +161,45 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
   if (st != ATTN_OK) return st;
   attn::DecodeArgs a{dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, n_splits, scale,
                      (float*)workspace, (hipStream_t)stream};
+  return hip_status(attn::launch_decode(a));
+}
+
+attn_status attn_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
+                              const int* block_table, const int* seq_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int d, int n_pages, int page_size,
+                              int max_pages, float scale, int n_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || n_pages <= 0 || page_size <= 0 ||
+      max_pages <= 0)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!paged_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (page_size % 32 != 0) return ATTN_ERR_VALUE;
+  // Keys per stream and elements per page stay in 32-bit index arithmetic.
+  if ((int64_t)max_pages * page_size >= (int64_t(1) << 31) || !sizes_ok(page_size, d))
+    return ATTN_ERR_SHAPE;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_VALUE;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, d, n_splits)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || !aligned16(workspace) || !aligned4(block_table) ||
+      !aligned4(seq_lens))
+    return ATTN_ERR_ALIGN;
+  const int es = esize(dtype);
+  const int64_t pool = (int64_t)n_pages * Hkv * page_size * d * es;
+  const Span ins[5] = {span(q, (int64_t)B * Hq * d * es), span(k_pages, pool),
+                       span(v_pages, pool), span(block_table, (int64_t)B * max_pages * 4),
+                       span(seq_lens, (int64_t)B * 4)};
+  const Span outs[3] = {span(o, (int64_t)B * Hq * d * es),
+                        lse ? span(lse, (int64_t)B * Hq * 4) : Span{0, 0},
+                        span(workspace, (int64_t)attn_decode_workspace_bytes(B, Hq, d, n_splits))};
+  attn_status st = check_alias(outs, 3, ins, 5);
+  if (st != ATTN_OK) return st;
+  attn::DecodeArgs a{dtype, q, k_pages, v_pages, o, lse, B, Hq, Hkv, 0, d, n_splits, scale,
+                     (float*)workspace, (hipStream_t)stream,
+                     attn::PagedKV{block_table, seq_lens, max_pages, page_size, n_pages}};
   return hip_status(attn::launch_decode(a));
 }
 

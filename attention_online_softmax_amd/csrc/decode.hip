@@ -365,11 +365,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 constexpr float kDecodeLazy = 8.f;  // lazy rescale threshold (log2 units), as in the forward
 constexpr int kDecodeHC = 8;        // query heads per work unit on the matrix cores
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ ws, int B, int Hq, int Hkv, int Skv,
-    int chunk, int n_splits, int n_hchunks, float scale_log2) {
+    int n_splits, int n_hchunks, float scale_log2, PagedKV pg) {
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TK = 32;  // keys per tile
@@ -396,10 +396,15 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
   // head then stream one contiguous window of K and V together, which the
   // memory system serves faster than as many separate streams.  Any
   // partition of the keys gives the same merged result.
-  const int tiles_total = (Skv + TK - 1) / TK;
+  //
+  // Paged caches: K and V are pools [n_pages, Hkv, page_size, d]; key t of
+  // stream b is row t % page_size of page table[b][t / page_size] (a page
+  // holds whole 32-key tiles), and stream b has lens[b] keys, clamped to
+  // the table's capacity.  A page id outside the pool reads as zeros.
   struct Unit {
     int split, hk, hc, b;
-    int L;   // tiles of this split
+    int keys;   // keys of the unit's stream
+    int L;      // tiles of this split
   };
   auto unit_of = [&](int u) {
     Unit x;
@@ -409,16 +414,38 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     r /= n_hchunks;
     x.hk = r % Hkv;
     x.b = r / Hkv;
-    x.L = x.split < tiles_total ? (tiles_total - x.split + n_splits - 1) / n_splits : 0;
+    x.keys = PAGED ? min(max(pg.lens[x.b], 0), pg.max_pages * pg.page_size) : Skv;
+    const int tiles = (x.keys + TK - 1) / TK;
+    x.L = x.split < tiles ? (tiles - x.split + n_splits - 1) / n_splits : 0;
     return x;
   };
   auto n_tiles = [&](const Unit& x) { return x.L; };
   auto tile_of = [&](const Unit& x, int t) { return x.split + t * n_splits; };
-  auto issue = [&](const Unit& x, int t, uint16_t* dK, uint16_t* dV) {
-    const int64_t base = (int64_t)(x.b * Hkv + x.hk) * Skv * D;
-    const int r0 = tile_of(x, t) * TK;
-    dma_tile<D, TK, 1>(K + base, dK, r0, Skv, 0, lane);
-    dma_tile<D, TK, 1>(V + base, dV, r0, Skv, 0, lane);
+  TileDma<D, TK, 1> pdma;   // paged tiles: one buffer descriptor per page
+  if constexpr (PAGED) pdma.init(0, lane);
+  // Page id of tile t of unit x, as a vector load (the address is made
+  // opaque per lane) so that the wait for it is the wait for the tiles in
+  // flight, issued one step before the id is needed.
+  auto load_pid = [&](const Unit& x, int t) -> int {
+    int z = lane;
+    asm volatile("" : "+v"(z));
+    const int page = tile_of(x, t) * TK / pg.page_size;   // < max_pages
+    return pg.table[(int64_t)x.b * pg.max_pages + page + (z >> 30)];
+  };
+  auto issue = [&](const Unit& x, int t, int pid, uint16_t* dK, uint16_t* dV) {
+    if constexpr (PAGED) {
+      const int p = __builtin_amdgcn_readfirstlane(pid);
+      const bool ok = p >= 0 && p < pg.n_pages;
+      const int64_t base = ((int64_t)(ok ? p : 0) * Hkv + x.hk) * pg.page_size * D;
+      const int r0 = tile_of(x, t) * TK % pg.page_size;
+      pdma.load(K + base, ok ? pg.page_size : 0, dK, r0, 0);
+      pdma.load(V + base, ok ? pg.page_size : 0, dV, r0, 0);
+    } else {
+      const int64_t base = (int64_t)(x.b * Hkv + x.hk) * Skv * D;
+      const int r0 = tile_of(x, t) * TK;
+      dma_tile<D, TK, 1>(K + base, dK, r0, Skv, 0, lane);
+      dma_tile<D, TK, 1>(V + base, dV, r0, Skv, 0, lane);
+    }
   };
   // Raw query rows of the unit's heads (lanes past the group's heads load a
   // valid row and are zeroed by q_keep when the rows are adopted, so that
@@ -480,7 +507,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c) qreg[c] &= keep;
   }
-  issue(cur, 0, sKa[wave], sVa[wave]);
+  issue(cur, 0, PAGED ? load_pid(cur, 0) : 0, sKa[wave], sVa[wave]);
   int t = 0;
   bool new_q = false;
   float m_ref = kNegInf, lpart = 0.f;
@@ -511,6 +538,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
       if (un < n_units) nxt = unit_of(un);
     }
     const bool more = un < n_units;
+    const bool go_on = !unit_end || more;
+    int pid = 0;
+    if (PAGED && go_on) pid = load_pid(nxt, tn);
 
     wait_vmcnt0();   // tile t (and every earlier load of this wave) has landed
     if (new_q) {
@@ -519,8 +549,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
       for (int c = 0; c < NDC; ++c) qreg[c] = qnext[c] & keep;
       new_q = false;
     }
-    if (!unit_end || more) {
-      issue(nxt, tn, nK, nV);
+    if (go_on) {
+      issue(nxt, tn, pid, nK, nV);
       if (unit_end) load_q(nxt, qnext);
     }
 
@@ -530,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
       s = mfma32(lds_row(cK, row_off<D>(r_off, c)), qreg[c] ^ qsign, s);
-    const int kvalid = Skv - tile_of(cur, t) * TK;  // keys of this tile that exist
+    const int kvalid = cur.keys - tile_of(cur, t) * TK;  // keys of this tile that exist
     float rmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -637,7 +667,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 #pragma unroll
       for (int c = 0; c < CPL; ++c) a[c] = fmaf(wj, v[j][c], a[c]);
     }
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;   // a stream with no keys: O = 0
     if constexpr (CPL == 1) {
       if constexpr (sizeof(T) == 4) {
         o[0] = a[0] * inv;
@@ -687,7 +717,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     }
   }
   l = group_reduce<64, false>(l);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   if constexpr (CPL == 1) {
     if constexpr (sizeof(T) == 4) {
       o[0] = a[0] * inv;
@@ -750,15 +780,20 @@ template <int D>
 static hipError_t launch_decode_mfma(const DecodeArgs& a) {
   const int G = a.Hq / a.Hkv;
   const int n_hchunks = (G + kDecodeHC - 1) / kDecodeHC;
-  const int chunk = (a.Skv + a.n_splits - 1) / a.n_splits;
   const int n_units = a.n_splits * a.Hkv * n_hchunks * a.B;
   // One workgroup (four waves) per compute unit, each wave a stream of units.
   const int wgs = (n_units + 3) / 4;
   const int grid = wgs < device_cus() ? wgs : device_cus();
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((decode_split_mfma_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws, a.B,
-                     a.Hq, a.Hkv, a.Skv, chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
+  if (a.pg.table)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<D, true>), dim3(grid), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
+                       a.B, a.Hq, a.Hkv, 0, a.n_splits, n_hchunks, a.scale * kLog2e, a.pg);
+  else
+    hipLaunchKernelGGL((decode_split_mfma_kernel<D, false>), dim3(grid), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
+                       a.B, a.Hq, a.Hkv, a.Skv, a.n_splits, n_hchunks, a.scale * kLog2e,
+                       PagedKV{nullptr, nullptr, 0, 0, 0});
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -776,6 +811,7 @@ static hipError_t dispatch_decode_d(const DecodeArgs& a) {
     if (a.d == 64) return launch_decode_mfma<64>(a);
     if (a.d == 128) return launch_decode_mfma<128>(a);
   }
+  if (a.pg.table) return hipErrorInvalidValue;   // paged caches: bf16, d 64 / 128 only
   switch (a.d) {
     case 64: return dispatch_decode_g<T, 64>(a);
     case 128: return dispatch_decode_g<T, 128>(a);

@@ -19,17 +19,27 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
+// Paged key/value cache: pools [n_pages, Hkv, page_size, d], a block table
+// [B, max_pages] of page ids and per-stream lengths [B], both in device
+// memory (table == nullptr: contiguous caches).
+struct PagedKV {
+  const int* table;
+  const int* lens;
+  int max_pages, page_size, n_pages;
+};
+
 struct DecodeArgs {
   int dtype;
   const void* q;
-  const void* k;
+  const void* k;  // [B, Hkv, Skv, d], or the key pool when paged
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, Skv, d, n_splits;
+  int B, Hq, Hkv, Skv, d, n_splits;  // Skv unused when paged
   float scale;
   float* ws;  // [n_splits, B, Hq] m, then l, then [n_splits, B, Hq, d] acc
   hipStream_t stream;
+  PagedKV pg;  // table == nullptr for contiguous caches
 };
 
 struct BwdArgs {

@@ -69,6 +69,13 @@ WORKLOADS = {
 }
 
 
+# Paged, variable-length decode at the grouped-query decode shape: the same
+# 8 streams of 4096 keys (B8 Hq32 Hkv8 d128), kept in 64-key pages handed
+# out in a seeded random order from a shared pool, 16 splits.
+PAGED_WORKLOAD = dict(B=8, Hq=32, Hkv=8, d=128, page_size=64, max_pages=64, lens=[4096] * 8,
+                      n_splits=16, seed=6000)
+
+
 def randn(shape, seed, mult=1.0, dtype=torch.bfloat16):
     """float32 N(0,1) from a CPU generator seeded with `seed`, times `mult`,
     rounded to `dtype`."""
@@ -90,6 +97,28 @@ def make_qkv(B, Hq, Hkv, Sq, Skv, d, dtype=torch.bfloat16, seed=0, mult=1.0, wit
     if with_do:
         out["do"] = randn((B, Hq, Sq, d), seed + 3, 1.0, dtype)
     return out
+
+
+def make_paged(B, Hq, Hkv, d, page_size, max_pages, lens, n_pages=None, dtype=torch.bfloat16,
+               seed=0, mult=1.0):
+    """Seeded paged-decode inputs: q [B,Hq,1,d]; key and value pools
+    [n_pages,Hkv,page_size,d] (default n_pages = B*max_pages + 3, so some
+    pages are unused); a block table [B,max_pages] int32 that hands out
+    distinct pool pages in a seeded random order; seq_lens [B] int32."""
+    if n_pages is None:
+        n_pages = B * max_pages + 3
+    if n_pages < B * max_pages:
+        raise ValueError("the pool must hold B * max_pages distinct pages")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 4)
+    table = torch.randperm(n_pages, generator=g)[:B * max_pages].to(torch.int32)
+    return {
+        "q": randn((B, Hq, 1, d), seed, mult, dtype),
+        "k_pages": randn((n_pages, Hkv, page_size, d), seed + 1, mult, dtype),
+        "v_pages": randn((n_pages, Hkv, page_size, d), seed + 2, mult, dtype),
+        "block_table": table.reshape(B, max_pages).contiguous(),
+        "seq_lens": torch.tensor(list(lens), dtype=torch.int32),
+    }
 
 
 def make_workload(w: Workload, seed_base=None):

@@ -78,7 +78,7 @@ int attn_abi_version(void);
 const char* attn_status_str(int status);
 
 /* Head dims compiled for (dtype, entry point): returns 1 if supported.
- * entry: 0 = attn_fwd, 1 = attn_decode, 2 = attn_bwd. */
+ * entry: 0 = attn_fwd, 1 = attn_decode, 2 = attn_bwd, 3 = attn_decode_paged. */
 int attn_supports(int dtype, int entry, int d);
 
 /*
@@ -131,6 +131,41 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         int B, int Hq, int Hkv, int Skv, int d, float scale, int n_splits,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Paged, variable-length split-KV decode: attn_decode over caches kept in
+ * fixed-size pages of a shared pool and found through a block table
+ * ("Don't Write Kernels, Derive Them", section "What happened": paged
+ * KV-cache access is among the operations that emerge from the same
+ * comprehensions); the result is attention of each stream's query over that
+ * stream's keys in order.
+ *   q           [B, Hq, 1, d]                         input
+ *   k_pages     [n_pages, Hkv, page_size, d]          input, key pool
+ *   v_pages     [n_pages, Hkv, page_size, d]          input, value pool
+ *   block_table [B, max_pages] int32, device memory   input: key t of stream b
+ *               is row t % page_size of page block_table[b][t / page_size]
+ *   seq_lens    [B] int32, device memory              input: keys per stream,
+ *               clamped to [0, max_pages * page_size]
+ *   o           [B, Hq, 1, d]                         output, dtype of q
+ *   lse         [B, Hq, 1] float32 (may be NULL)      output
+ *   workspace   >= attn_decode_workspace_bytes(B, Hq, d, n_splits) bytes,
+ *               16-byte aligned; contents on entry ignored, on exit unspecified.
+ * The table and the lengths are read by the kernels, never by the host: a
+ * page id outside [0, n_pages) reads as a page of zero keys and values (no
+ * memory outside the pools is touched), and a stream with no keys gets
+ * O = 0 and lse = -inf.  Split s of a stream takes its 32-key tiles s,
+ * s + n_splits, ...; the splits are merged as in attn_decode.
+ * bf16 only, d in {64, 128} (else ATTN_ERR_UNSUPPORTED); page_size a
+ * multiple of 32 (else ATTN_ERR_VALUE); max_pages * page_size < 2^31 (else
+ * ATTN_ERR_SHAPE); block_table and seq_lens 4-byte aligned, the other
+ * pointers 16-byte aligned; 1 <= n_splits <= 256.  Two kernels, as
+ * attn_decode.
+ */
+attn_status attn_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
+                              const int* block_table, const int* seq_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int d, int n_pages, int page_size,
+                              int max_pages, float scale, int n_splits, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Workspace for attn_bwd: 2 * B * Hq * Sqp float32 values, Sqp = Sq rounded
  * up to a multiple of 32 (per query row D_i = dO_i . O_i and
  * -lse_i * log2(e), with rows past Sq padded), rounded up to 256 bytes.
@@ -165,7 +200,8 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
  * point records events[2i] on its stream just before the i-th kernel it
  * launches and events[2i+1] just after it, for 2i+1 < n; the caller reads
  * the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
- * (the forward kernel), attn_decode 2 (split, combine), attn_bwd 2
+ * (the forward kernel), attn_decode and attn_decode_paged 2 (split,
+ * combine), attn_bwd 2
  * (dQ together with D = rowsum(dO*O), then dK/dV).  Pass NULL or n = 0 to stop.  The library
  * neither creates nor destroys the events.  Returns ATTN_ERR_VALUE if n < 0.
  */

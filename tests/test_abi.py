@@ -50,6 +50,8 @@ def test_supports():
         assert aos.attn_supports(F32, 1, d) and aos.attn_supports(BF16, 1, d)
     assert aos.attn_supports(BF16, 2, 64) and aos.attn_supports(BF16, 2, 128)
     assert not aos.attn_supports(BF16, 2, 256)
+    assert aos.attn_supports(BF16, 3, 64) and aos.attn_supports(BF16, 3, 128)
+    assert not aos.attn_supports(BF16, 3, 256) and not aos.attn_supports(F32, 3, 128)
     assert not aos.attn_supports(BF16, 0, 96)
     assert not aos.attn_supports(7, 0, 64)
 
@@ -127,6 +129,44 @@ def test_decode_validation():
     assert call(ws=k) == ALIAS
     assert call(o=q) == ALIAS
     assert call(scale=float("-inf")) == VALUE
+
+
+def test_decode_paged_validation():
+    f = Fake()
+    q, kp, vp, tab, lens, o, lse, ws = (f() for _ in range(8))
+    need = aos.attn_decode_workspace_bytes(2, 8, 128, 16)
+    L = aos.lib()
+
+    def call(**kw):
+        a = dict(dt=BF16, q=q, kp=kp, vp=vp, tab=tab, lens=lens, o=o, lse=lse, B=2, Hq=8, Hkv=2,
+                 d=128, npg=64, ps=64, mp=32, scale=0.1, n=16, ws=ws, wsb=need)
+        a.update(kw)
+        return L.attn_decode_paged(a["dt"], a["q"], a["kp"], a["vp"], a["tab"], a["lens"],
+                                   a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["npg"],
+                                   a["ps"], a["mp"], a["scale"], a["n"], a["ws"], a["wsb"], None)
+
+    assert call(tab=None) == NULL
+    assert call(lens=None) == NULL
+    assert call(kp=None) == NULL
+    assert call(npg=0) == SHAPE
+    assert call(mp=0) == SHAPE
+    assert call(ps=0) == SHAPE
+    assert call(Hq=6, Hkv=4) == SHAPE
+    assert call(dt=F32) == UNSUP
+    assert call(d=256) == UNSUP
+    assert call(ps=48) == VALUE                      # pages hold whole 32-key tiles
+    assert call(mp=1 << 26, ps=64) == SHAPE          # 2^32 keys per stream
+    assert call(n=0) == VALUE
+    assert call(n=257) == VALUE
+    assert call(scale=float("nan")) == VALUE
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(tab=tab + 2) == ALIGN
+    assert call(lens=lens + 1) == ALIGN
+    assert call(q=q + 8) == ALIGN
+    assert call(o=kp) == ALIAS
+    assert call(ws=tab) == ALIAS
+    assert call(lse=vp + 64) == ALIAS
 
 
 def test_bwd_validation():
