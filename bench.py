@@ -3,7 +3,8 @@
 One step = attn_fwd followed by attn_bwd on the training workload
 (bf16, causal, B=4, H=16, S=2048, d=128): every row of the path except
 split-KV decode, which is timed in the same run on its own workload
-(bf16, B=8, Hq=32, Hkv=8, Skv=4096, d=128, 16 splits), as is the 44k-token
+(bf16, B=8, Hq=32, Hkv=8, Skv=4096, d=128, 16 splits), as are the same
+decode over a paged cache (shuffled 64-key pages) and the 44k-token
 head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
 resident in device memory; three input sets rotate so that no step reuses
 the previous step's data from the 256 MiB last-level cache.
@@ -15,13 +16,14 @@ timed with HIP events recorded around that kernel inside the timed region.
 `cpu_baseline` times the float64 oracle on a bounded sample on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only fwd_bwd|decode|prefill]
+                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill]
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -349,6 +351,44 @@ def bench_decode(args, hev, stream, reps):
             "algorithmic_bytes": algo, "kernels": ks}
 
 
+def bench_decode_paged(args, hev, stream, reps):
+    """The paged, variable-length decode at the grouped-query decode shape
+    (same streams and bytes as gqa_decode, keys in shuffled 64-key pages)."""
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import PAGED_WORKLOAD as w, make_paged
+    sets = [{k: v.cuda() for k, v in make_paged(w["B"], w["Hq"], w["Hkv"], w["d"], w["page_size"],
+                                                 w["max_pages"], w["lens"],
+                                                 seed=w["seed"] + 100 * i).items()}
+            for i in range(3)]
+    ws = torch.empty(aos.attn_decode_workspace_bytes(w["B"], w["Hq"], w["d"], w["n_splits"]),
+                     device="cuda", dtype=torch.uint8)
+    outs = [(torch.empty_like(s["q"]), torch.empty((w["B"], w["Hq"], 1), device="cuda",
+                                                   dtype=torch.float32)) for s in sets]
+    scale = 1.0 / math.sqrt(w["d"])
+
+    def dec(i):
+        s, (o, lse) = sets[i % 3], outs[i % 3]
+        aos.attn_decode_paged(s["q"], s["k_pages"], s["v_pages"], s["block_table"], s["seq_lens"],
+                              scale=scale, n_splits=w["n_splits"], o=o, lse=lse, workspace=ws)
+
+    for i in range(5):
+        dec(i)
+    total_ms, _, spans = run_calls([("decode", dec)], {"decode": 2}, hev, reps, stream,
+                                   slots={"decode": {0, 3}})
+    q = quantiles(spans["decode"])
+    keys = sum(w["lens"])
+    algo = (2.0 * keys * w["Hkv"] * w["d"] * 2 + 2.0 * w["B"] * w["Hq"] * w["d"] * 2
+            + w["B"] * w["Hq"] * 4 + w["B"] * (w["max_pages"] + 1) * 4)
+    return {"workload": "paged_decode: bf16, B8 Hq32 Hkv8 d128, 4096 keys per stream in "
+                        "shuffled 64-key pages, 16 splits",
+            "us_median": q["median"] * 1e3, "us_p10": q["p10"] * 1e3, "us_p90": q["p90"] * 1e3,
+            "us_per_call_issued_back_to_back": total_ms / reps * 1e3,
+            "GB/s": algo / (q["median"] * 1e-3) / 1e9,
+            "frac_of_8TBs": algo / (q["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes": algo}
+
+
 def bench_prefill(args, hev, stream, reps):
     import torch
     import attention_online_softmax_amd as aos
@@ -380,7 +420,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd_bwd", "decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill"],
+                    default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -400,6 +441,9 @@ def main():
     if args.only == "decode":
         print(json.dumps(bench_decode(args, hev, stream, args.steps)), flush=True)
         return
+    if args.only == "paged_decode":
+        print(json.dumps(bench_decode_paged(args, hev, stream, args.steps)), flush=True)
+        return
     if args.only == "prefill":
         print(json.dumps(bench_prefill(args, hev, stream, args.steps)), flush=True)
         return
@@ -412,6 +456,9 @@ def main():
         extras["decode"] = bench_decode(args, hev, stream, max(args.steps, 50))
         print(f"[bench] decode: {extras['decode']['us_median']:.1f} us", file=sys.stderr,
               flush=True)
+        extras["paged_decode"] = bench_decode_paged(args, hev, stream, max(args.steps, 50))
+        print(f"[bench] paged decode: {extras['paged_decode']['us_median']:.1f} us",
+              file=sys.stderr, flush=True)
         extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
         print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",
               file=sys.stderr, flush=True)
