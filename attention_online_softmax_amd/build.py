@@ -3,8 +3,9 @@
 Usage: python -m attention_online_softmax_amd.build   (or build() from Python)
 
 Every .hip/.cpp file under csrc/ is compiled by hipcc to an object, in
-parallel, then linked into attention_online_softmax_amd/libattn.so.  Packed
-fp32 VALU instructions are disabled for all device code.
+parallel, then linked into attention_online_softmax_amd/libattn.so; the
+benchmark's measured-ceiling kernels (ceilings/) become libceilings.so.
+Packed fp32 VALU instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -75,7 +76,28 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_ceilings(verbose)
     return LIB
+
+
+CEIL_SRC = os.path.join(PKG, "ceilings", "ceilings.hip")
+CEIL_LIB = os.path.join(PKG, "ceilings", "libceilings.so")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """The benchmark's measured-ceiling kernels (streaming read, MFMA loop),
+    a library of their own that the attention library does not link."""
+    tmp = CEIL_LIB + ".tmp"
+    cmd = [hipcc()] + device_flags() + ["-shared", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEIL_SRC}:\n{out}")
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB
 
 
 if __name__ == "__main__":

@@ -389,6 +389,59 @@ def bench_decode_paged(args, hev, stream, reps):
             "algorithmic_bytes": algo}
 
 
+def measured_ceilings(stream):
+    """What the box reaches, as the measured ceilings beside the spec peaks:
+    HBM read bandwidth of a grid-stride streaming read of 1 GiB (three
+    buffers rotate, so no pass is served by the 256 MiB last-level cache)
+    and the bf16 matrix-core rate of 32x32x16 MFMAs fed from registers at two
+    waves per SIMD (kernels in attention_online_softmax_amd/ceilings/)."""
+    import ctypes
+    import torch
+    from attention_online_softmax_amd.build import CEIL_LIB
+    L = ctypes.CDLL(CEIL_LIB)
+    L.ceil_read_run.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_void_p]
+    L.ceil_mfma_run.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    nbytes, blocks = 1 << 30, 1024
+    bufs = [torch.ones(nbytes // 4, device="cuda", dtype=torch.int32) for _ in range(3)]
+    out = torch.empty(blocks * 256, device="cuda", dtype=torch.float32)
+
+    def read(i):
+        rc = L.ceil_read_run(ctypes.c_void_p(bufs[i % 3].data_ptr()), nbytes,
+                             ctypes.c_void_p(out.data_ptr()), blocks, st)
+        if rc:
+            raise RuntimeError(f"ceil_read_run: hip error {rc}")
+
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    read_gbs = nbytes / timed(read, 12) / 1e9
+    del bufs
+    mblocks, iters = 512, 4000
+
+    def mf(i):
+        rc = L.ceil_mfma_run(ctypes.c_void_p(out.data_ptr()), mblocks, iters, st)
+        if rc:
+            raise RuntimeError(f"ceil_mfma_run: hip error {rc}")
+
+    mfma_tf = mblocks * 4 * iters * 16 * 32768.0 / timed(mf, 5) / 1e12
+    return {"hbm_read_GB/s": read_gbs,
+            "hbm_read_kind": "grid-stride 16-byte loads over 1 GiB, 3 rotating buffers",
+            "bf16_mfma_TFLOP/s": mfma_tf,
+            "bf16_mfma_kind": "32x32x16 bf16 MFMAs from registers, 4 chains, 2 waves/SIMD",
+            "spec_hbm_GB/s": PEAK_HBM_GBS, "spec_bf16_TFLOP/s": PEAK_BF16_TFLOPS}
+
+
 def bench_prefill(args, hev, stream, reps):
     import torch
     import attention_online_softmax_amd as aos
@@ -501,6 +554,21 @@ def main():
         "kernels": ks,
     }
     line.update(extras)
+    if not args.no_extras and args.only is None:
+        c = measured_ceilings(stream)
+        c["roofline_frac_of_measured"] = roofline["achieved"] / (
+            c["bf16_mfma_TFLOP/s"] if roofline["bound"] == "mfma" else c["hbm_read_GB/s"])
+        if "decode" in line:
+            c["decode_frac_of_measured_read"] = line["decode"]["GB/s"] / c["hbm_read_GB/s"]
+        if "paged_decode" in line:
+            c["paged_decode_frac_of_measured_read"] = (line["paged_decode"]["GB/s"]
+                                                       / c["hbm_read_GB/s"])
+        if "long_prefill" in line:
+            c["long_prefill_frac_of_measured_mfma"] = (line["long_prefill"]["TFLOP/s"]
+                                                       / c["bf16_mfma_TFLOP/s"])
+        line["measured_ceilings"] = c
+        print(f"[bench] measured ceilings: read {c['hbm_read_GB/s']:.0f} GB/s, "
+              f"bf16 MFMA {c['bf16_mfma_TFLOP/s']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
     hev.destroy()
 
