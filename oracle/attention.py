@@ -27,6 +27,10 @@ Readings where the pages are silent (each is also listed in the design notes):
 * causal alignment for Sq != Skv is bottom-right: key j is allowed for query
   i iff j <= i + (Skv - Sq); causal with Sq > Skv would leave a row with no
   allowed key, which the definition excludes;
+* a sliding window of W keys (W > 0, causal only) is one more pattern of the
+  additive mask C: key j is allowed for query i iff
+  i + (Skv - Sq) - W < j <= i + (Skv - Sq), so every row keeps its diagonal
+  key; W <= 0 means no window;
 * grouped-query heads: query head h reads key/value head h // (Hq // Hkv);
 * LSE is the natural-log log-sum-exp of the scaled, masked scores, m + ln l;
 * the scale multiplies the exact dot product;
@@ -86,17 +90,23 @@ def allowed_keys(i, Sq, Skv, causal):
     return min(n, Skv)
 
 
-def mask_matrix(rows, Sq, Skv, causal):
-    """Additive mask C restricted to the given query rows: 0 or -inf."""
+def mask_matrix(rows, Sq, Skv, causal, window=0):
+    """Additive mask C restricted to the given query rows: 0 or -inf.  With
+    window W > 0 (causal only), keys more than W - 1 before the diagonal are
+    masked too."""
+    if window > 0 and not causal:
+        raise ValueError("a sliding window needs the causal mask")
     rows = np.asarray(rows)
     c = np.zeros((rows.size, Skv))
     if causal:
         j = np.arange(Skv)[None, :]
         c[j > rows[:, None] + (Skv - Sq)] = NEG_INF
+        if window > 0:
+            c[j <= rows[:, None] + (Skv - Sq) - window] = NEG_INF
     return c
 
 
-def scores(q, k, causal, scale, b, hq, rows=None):
+def scores(q, k, causal, scale, b, hq, rows=None, window=0):
     """S = Q K^T * scale + C for one (batch, query head), selected rows."""
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -104,10 +114,10 @@ def scores(q, k, causal, scale, b, hq, rows=None):
     if rows is None:
         rows = np.arange(Sq)
     s = (q[b, hq][rows] @ k[b, hq // g].T) * scale
-    return s + mask_matrix(rows, Sq, Skv, causal)
+    return s + mask_matrix(rows, Sq, Skv, causal, window)
 
 
-def attention_ref(q, k, v, causal, scale, rows=None):
+def attention_ref(q, k, v, causal, scale, rows=None, window=0):
     """Scaled dot-product attention, the plain definition.
 
     Follows the first display equation of "Compilers and Kernels", section
@@ -117,6 +127,7 @@ def attention_ref(q, k, v, causal, scale, rows=None):
 
     rows: optional sorted array of query-row indices; when given, only those
     rows are computed and O is [B, Hq, len(rows), dv], LSE [B, Hq, len(rows)].
+    window: sliding-window width W (causal only; <= 0: none).
     Returns (O, LSE).
     """
     B, Hq, Hkv, Sq, Skv, d, dv = _check_shapes(q, k, v)
@@ -131,7 +142,7 @@ def attention_ref(q, k, v, causal, scale, rows=None):
             vv = v[b, h // g]
             for r0 in range(0, rows.size, _ROW_BLOCK):
                 rr = rows[r0:r0 + _ROW_BLOCK]
-                s = scores(q, k, causal, scale, b, h, rr)
+                s = scores(q, k, causal, scale, b, h, rr, window)
                 m = s.max(axis=1)
                 e = np.exp(s - m[:, None])
                 l = e.sum(axis=1)
@@ -232,7 +243,7 @@ def online_softmax_recurrence(s, v, block):
     return o / l[:, None], m + np.log(l)
 
 
-def attention_monoid(q, k, v, causal, scale, boundaries, tree=None):
+def attention_monoid(q, k, v, causal, scale, boundaries, tree=None, window=0):
     """Attention as a fold of key-block states under `merge`.
 
     boundaries: increasing key offsets starting at 0 and ending at Skv that
@@ -249,7 +260,7 @@ def attention_monoid(q, k, v, causal, scale, boundaries, tree=None):
     lse = np.empty((B, Hq, Sq))
     for b in range(B):
         for h in range(Hq):
-            s = scores(q, k, causal, scale, b, h)
+            s = scores(q, k, causal, scale, b, h, window=window)
             vv = v[b, h // g]
             states = [block_state(s[:, a:z], vv[a:z])
                       for a, z in zip(boundaries[:-1], boundaries[1:])]
@@ -378,7 +389,7 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, scale):
 # section: the backward recomputes local score and probability tiles).
 # ---------------------------------------------------------------------------
 
-def attention_bwd_ref(q, k, v, do, causal, scale, lse=None):
+def attention_bwd_ref(q, k, v, do, causal, scale, lse=None, window=0):
     """Gradients of O = softmax(scale Q K^T + C) V with respect to Q, K, V.
 
     lse: [B, Hq, Sq] saved forward statistic; computed from the definition
@@ -389,7 +400,7 @@ def attention_bwd_ref(q, k, v, do, causal, scale, lse=None):
         raise ValueError("causal with Sq > Skv leaves a query row with no allowed key")
     g = Hq // Hkv
     if lse is None:
-        _, lse = attention_ref(q, k, v, causal, scale)
+        _, lse = attention_ref(q, k, v, causal, scale, window=window)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dvv = np.zeros_like(v)
@@ -397,7 +408,7 @@ def attention_bwd_ref(q, k, v, do, causal, scale, lse=None):
     for b in range(B):
         for h in range(Hq):
             kk, vv = k[b, h // g], v[b, h // g]
-            s = scores(q, k, causal, scale, b, h)
+            s = scores(q, k, causal, scale, b, h, window=window)
             p = np.exp(s - lse[b, h][:, None])          # masked pairs: exp(-inf) = 0
             dp = do[b, h] @ vv.T
             D = (p * dp).sum(axis=1)

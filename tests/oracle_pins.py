@@ -215,6 +215,60 @@ def pin_fwd_torch_sdpa(A):
         _close(O, ref.numpy(), 1e-13, "torch sdpa O")
 
 
+def pin_fwd_window(A):
+    """Sliding windows of W keys ending at the diagonal: 50-digit brute force
+    over exactly the keys j with i + off - W < j <= i + off; torch float64
+    sdpa with that boolean mask; W = 1 selects the diagonal key (O = V,
+    LSE = scale q . k); W at least Skv is the plain causal mask."""
+    for seed, (B, Hq, Hkv, Sq, Skv, d), W in [(50, (1, 2, 1, 6, 6, 3), 3),
+                                              (51, (1, 2, 2, 4, 9, 2), 4)]:
+        q = _rand(seed, B, Hq, Sq, d)
+        k = _rand(seed + 10, B, Hkv, Skv, d)
+        v = _rand(seed + 20, B, Hkv, Skv, d)
+        O, L = A.attention_ref(q, k, v, True, 0.6, window=W)
+        mpmath.mp.dps = 50
+        g = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(Sq):
+                    hi = i + Skv - Sq
+                    js = range(max(0, hi - W + 1), hi + 1)
+                    es = [mpmath.exp(mpmath.mpf(0.6) * mpmath.fsum(
+                        mpmath.mpf(q[b, h, i, c]) * mpmath.mpf(k[b, h // g, j, c])
+                        for c in range(d))) for j in js]
+                    den = mpmath.fsum(es)
+                    for c in range(d):
+                        num = mpmath.fsum(e * mpmath.mpf(v[b, h // g, j, c]) for e, j in zip(es, js))
+                        _close(O[b, h, i, c], float(num / den), 1e-13, "window mpmath O")
+                    _close(L[b, h, i], float(mpmath.log(den)), 1e-13, "window mpmath LSE")
+    B, Hq, Hkv, Sq, Skv, d = 2, 4, 2, 11, 17, 8
+    q = _rand(52, B, Hq, Sq, d)
+    k = _rand(53, B, Hkv, Skv, d)
+    v = _rand(54, B, Hkv, Skv, d)
+    scale = 1 / math.sqrt(d)
+    kt = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1)
+    i = torch.arange(Sq)[:, None]
+    j = torch.arange(Skv)[None, :]
+    for W in (1, 2, 5, Skv - 1):
+        O, L = A.attention_ref(q, k, v, True, scale, window=W)
+        mask = (j <= i + (Skv - Sq)) & (j > i + (Skv - Sq) - W)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), kt, vt, attn_mask=mask, scale=scale)
+        _close(O, ref.numpy(), 1e-13, f"window {W} torch sdpa O")
+    O, L = A.attention_ref(q, k, v, True, scale, window=1)
+    diag = np.arange(Sq) + (Skv - Sq)
+    g = Hq // Hkv
+    for h in range(Hq):
+        _close(O[:, h], v[:, h // g, diag], 1e-14, "window 1 O")
+        _close(L[:, h], scale * np.einsum("bid,bid->bi", q[:, h], k[:, h // g, diag]), 1e-14,
+               "window 1 LSE")
+    Oc, Lc = A.attention_ref(q, k, v, True, scale)
+    for W in (Skv, Skv + 5):
+        O, L = A.attention_ref(q, k, v, True, scale, window=W)
+        assert np.array_equal(O, Oc) and np.array_equal(L, Lc), "window >= Skv is causal"
+
+
 def pin_fwd_invariants(A):
     """Key shift moves LSE by scale q.u and keeps O; joint (K, V) row
     permutation keeps O (non-causal); grouped heads equal repeated heads."""
@@ -512,6 +566,24 @@ def pin_bwd_autograd(A):
         _close(dk, kt.grad.numpy(), 1e-12, "autograd dK")
         _close(dv, vt.grad.numpy(), 1e-12, "autograd dV")
         _close(D, np.sum(do * o.detach().numpy(), axis=-1), 1e-12, "D = rowsum(dO*O)")
+    # sliding windows (causal)
+    i = torch.arange(Sq)[:, None]
+    j = torch.arange(Skv)[None, :]
+    for W in (1, 3, 8):
+        qt = torch.from_numpy(q).requires_grad_()
+        kt = torch.from_numpy(k).requires_grad_()
+        vt = torch.from_numpy(v).requires_grad_()
+        kr = kt.repeat_interleave(Hq // Hkv, dim=1)
+        vr = vt.repeat_interleave(Hq // Hkv, dim=1)
+        s = (qt @ kr.transpose(-1, -2)) * scale
+        keep = (j <= i + (Skv - Sq)) & (j > i + (Skv - Sq) - W)
+        s = s.masked_fill(~keep, float("-inf"))
+        o = torch.softmax(s, dim=-1) @ vr
+        o.backward(torch.from_numpy(do))
+        dq, dk, dv, D = A.attention_bwd_ref(q, k, v, do, True, scale, window=W)
+        _close(dq, qt.grad.numpy(), 1e-12, f"window {W} autograd dQ")
+        _close(dk, kt.grad.numpy(), 1e-12, f"window {W} autograd dK")
+        _close(dv, vt.grad.numpy(), 1e-12, f"window {W} autograd dV")
 
 
 def pin_bwd_golden(A):
@@ -554,7 +626,8 @@ def pin_bwd_identities(A):
 
 
 FORWARD_PINS = [pin_fwd_mpmath, pin_fwd_golden, pin_fwd_uniform, pin_fwd_onehot,
-                pin_fwd_single_key, pin_fwd_scipy, pin_fwd_torch_sdpa, pin_fwd_invariants]
+                pin_fwd_single_key, pin_fwd_scipy, pin_fwd_torch_sdpa, pin_fwd_window,
+                pin_fwd_invariants]
 MONOID_PINS = [pin_monoid_golden, pin_monoid_identity, pin_monoid_chunkings, pin_monoid_lse]
 DECODE_PINS = [pin_decode, pin_decode_paged]
 BACKWARD_PINS = [pin_bwd_finite_difference, pin_bwd_autograd, pin_bwd_golden, pin_bwd_identities]

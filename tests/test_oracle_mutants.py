@@ -44,6 +44,12 @@ MUTANTS = [
     ("split chunk floor", "c = -(-Skv // n_splits)", "c = max(Skv // n_splits, 1)", 0),
     ("decode without scale", "s = (q[b, h] @ k[b, h // g].T) * scale",
      "s = (q[b, h] @ k[b, h // g].T)", 0),
+    ("window off by one", "c[j <= rows[:, None] + (Skv - Sq) - window] = NEG_INF",
+     "c[j < rows[:, None] + (Skv - Sq) - window] = NEG_INF", 0),
+    ("window ignored", "        if window > 0:\n            c[j <=",
+     "        if window < 0:\n            c[j <=", 0),
+    ("window top-left aligned", "c[j <= rows[:, None] + (Skv - Sq) - window] = NEG_INF",
+     "c[j <= rows[:, None] - window] = NEG_INF", 0),
     ("paged row within page", "out[ok] = pages[pid[ok], :, (t % ps)[ok], :]",
      "out[ok] = pages[pid[ok], :, ((t + 1) % ps)[ok], :]", 0),
     ("paged page of next key", "pid = np.asarray(block_table[b])[t // ps]",
