@@ -52,7 +52,7 @@ def lib():
     L.attn_supports.restype = i
     L.attn_supports.argtypes = [i, i, i]
     L.attn_fwd.restype = i
-    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode.restype = i
@@ -64,7 +64,7 @@ def lib():
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_bwd.restype = i
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                           i, i, i, i, i, i, i, f, vp, sz, vp]
+                           i, i, i, i, i, i, i, i, f, vp, sz, vp]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -132,8 +132,10 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, want_lse=True):
-    """Forward prefill.  q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d]; returns (o, lse)."""
+def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, want_lse=True,
+             window=0):
+    """Forward prefill.  q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d]; returns (o, lse).
+    window > 0 (with causal): a sliding window of that many keys."""
     _check([q, k, v], ["q", "k", "v"])
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -145,7 +147,7 @@ def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, w
         lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
     dt = _dtype_code(q)
     st = lib().attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                        B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), float(scale),
+                        B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), int(window), float(scale),
                         _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_fwd")
@@ -214,8 +216,8 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, n_
 
 
 def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
-    """Backward.  Returns (dq, dk, dv)."""
+             workspace=None, stream=None, window=0):
+    """Backward (same causal / window as the forward call).  Returns (dq, dk, dv)."""
     _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -229,7 +231,7 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
         workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
     st = lib().attn_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                         _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
-                        int(bool(causal)), float(scale), _ptr(workspace),
+                        int(bool(causal)), int(window), float(scale), _ptr(workspace),
                         workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_bwd")

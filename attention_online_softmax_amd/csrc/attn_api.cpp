@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxSplits = 256;
 
 struct Span {
@@ -107,12 +107,13 @@ int attn_supports(int dtype, int entry, int d) {
 }
 
 attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
-                     void* stream) {
+                     int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
+                     float scale, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (window > 0 && !causal) return ATTN_ERR_VALUE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   if (!fwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
@@ -125,8 +126,8 @@ attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
                         lse ? span(lse, (int64_t)B * Hq * Sq * 4) : Span{0, 0}};
   attn_status st = check_alias(outs, 2, ins, 3);
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{dtype, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0, scale,
-                  (hipStream_t)stream};
+  attn::FwdArgs a{dtype, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0,
+                  window > 0 ? window : 0, scale, (hipStream_t)stream};
   return hip_status(attn::launch_fwd(a));
 }
 
@@ -211,12 +212,13 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d) {
 
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
                      const void* d_o, const float* lse, void* dq, void* dk, void* dv, int B,
-                     int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
+                     float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (window > 0 && !causal) return ATTN_ERR_VALUE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   // The kernels address the workspace with 32-bit byte offsets.
   if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
@@ -236,7 +238,8 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   attn_status st = check_alias(outs, 4, ins, 6);
   if (st != ATTN_OK) return st;
   attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
-                  causal ? 1 : 0, scale, (float*)workspace, (hipStream_t)stream};
+                  causal ? 1 : 0, window > 0 ? window : 0, scale, (float*)workspace,
+                  (hipStream_t)stream};
   return hip_status(attn::launch_bwd(a));
 }
 

@@ -55,8 +55,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale,
-    float scale_log2, int64_t rows_pad) {
+    uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
+    float scale, float scale_log2, int64_t rows_pad) {
   constexpr int QT = 32;   // query rows per tile
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -86,9 +86,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
 
-  // Queries that can see any key of this tile: i >= first_key - off.
+  // Queries that can see any key of this tile: i >= first_key - off, and
+  // with a sliding window of `window` keys (causal only, 0 = none) also
+  // i < last_key - off + window.
+  const bool win = CAUSAL && window > 0;
   const int q_start = CAUSAL ? (max(0, ktile * 128 - off) / QT) * QT : 0;
-  const int n_qt = (Sq - q_start + QT - 1) / QT;   // query tiles per head (>= 1)
+  const int q_end = win ? min(Sq, ktile * 128 + 127 - off + window) : Sq;
+  // Query tiles per head; 0 when no query's window reaches these keys
+  // (possible only with a window and Sq < Skv).
+  const int n_qt = max(0, (q_end - q_start + QT - 1) / QT);
   const int n_it = G * n_qt;
 
   // The workgroup's V rows (rows past Skv arrive as zeros).
@@ -158,8 +164,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     }
     // The softmax step and the products in two halves of 16 queries, so only
     // half of P and dS is live at a time.
-    const bool masked = CAUSAL && key0_wave + 31 > qs + off;
-    const int lo = key - off - qs - 8 * g;   // causal: element (c, j) visible iff 16c + j >= lo
+    const bool masked = (CAUSAL && key0_wave + 31 > qs + off) ||
+                        (win && key0_wave < qs + QT + off - window);
+    // Element (c, j) is query qs + 16c + 8g + j: visible iff lo <= 16c + j
+    // (causal) and 16c + j <= hi (window).
+    const int lo = key - off - qs - 8 * g;
+    const int hi = win ? lo + window - 1 : 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       u32x4 pb, dsb;
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
           const float dd = dn[j >> 1][2 * (j & 1)];
           const float nl = dn[j >> 1][2 * (j & 1) + 1];
           float p = fast_exp2(fmaf(s[i], scale_log2, nl));
-          if constexpr (decltype(msk)::value) p = (16 * c + j >= lo) ? p : 0.f;
+          if constexpr (decltype(msk)::value) p = (16 * c + j >= lo && 16 * c + j <= hi) ? p : 0.f;
           pv[j] = p;
           dsv[j] = p * (dp[i] - dd);
         }
@@ -206,8 +216,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     issue(nxt);
     const int qs = q_start + cur_qt * QT;
     if (++cur_qt == n_qt) cur_qt = 0;
-    // Tiles whose queries all precede this wave's first visible key: skip.
+    // Tiles whose queries all precede this wave's first visible key, or
+    // whose windows all start after its last key: skip.
     if (CAUSAL && qs + QT - 1 + off < key0_wave) return;
+    if (win && qs + off - window + 1 > key0_wave + 31) return;
     step(cur, qs);
   };
 #pragma clang loop unroll(disable)
@@ -215,6 +227,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     body(sT0, sT1);
     if (i + 1 < n_it) body(sT1, sT0);
   }
+  wait_vmcnt0();   // nothing in flight into LDS when the workgroup ends (n_it may be 0)
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
   store_transposed<NDB>(dK + kro, dkt, g, scale);
@@ -243,7 +256,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
     const float* __restrict__ LSE, float* __restrict__ ws, uint16_t* __restrict__ dQ, int BH,
-    int Hq, int Hkv, int Sq, int Sqp, int Skv, float scale, float scale_log2, int n_qtiles) {
+    int Hq, int Hkv, int Sq, int Sqp, int Skv, int window, float scale, float scale_log2,
+    int n_qtiles) {
   constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -270,12 +284,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int last_row = min(qtile * 128 + 128, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
+  // Sliding window of `window` keys (causal only, 0 = none): row i sees
+  // keys [i + off - window + 1, i + off]; the loop starts at the first tile
+  // the workgroup's first row can see.
+  const bool win = CAUSAL && window > 0;
+  const int t0 = win ? max(0, qtile * 128 + off - window + 1) / BC : 0;
 
   // K/V tiles through buffer loads; rows past Skv arrive as zeros (masked).
   TileDma<D, BC, 4> dma;
   dma.init(wave, lane);
-  dma.load(Kh, Skv, sK0, 0, wave);
-  dma.load(Vh, Skv, sV0, 0, wave);
+  dma.load(Kh, Skv, sK0, t0 * BC, wave);
+  dma.load(Vh, Skv, sV0, t0 * BC, wave);
 
   const int qrow = min(row, Sq - 1);
   const uint16_t* Qr = Q + ((int64_t)bh * Sq + qrow) * D;
@@ -309,8 +328,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqt[db][i] = 0.f;
 
-  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
+  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [row_lo, row_limit)
+  const int row_lo = win ? row + off - window + 1 : 0;
   const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
+  const int wave_kv_first = win ? wave_row0 + off - window + 1 : 0;
+  const int wave_lo_max = win ? min(wave_row0 + 31, Sq - 1) + off - window + 1 : 0;
   int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
@@ -328,8 +350,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
       const int ks = k0 + kb * 32;
-      if (ks > wave_kv_last) continue;
-      const bool need_mask = (ks + 32 > Skv) || (CAUSAL && ks + 31 > wave_row0 + off);
+      if (ks > wave_kv_last || ks + 31 < wave_kv_first) continue;
+      const bool need_mask = (ks + 32 > Skv) || (CAUSAL && ks + 31 > wave_row0 + off) ||
+                             (win && ks < wave_lo_max);
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
@@ -355,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
               float p = fast_exp2(fmaf(s[i], scale_log2, nl));
               if constexpr (decltype(masked)::value) {
                 const int kk = ks + 16 * c + 8 * g + 2 * j + u;
-                p = (kk < row_limit) ? p : 0.f;
+                p = (kk < row_limit && kk >= row_lo) ? p : 0.f;
               }
               dsv[u] = p * (dp[i] - dd);
             }
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
   };
 #pragma clang loop unroll(disable)
-  for (int tt = 0; tt < n_tiles; tt += 2) {
+  for (int tt = t0; tt < n_tiles; tt += 2) {
     step(sK0, sV0, sK1, sV1, tt);
     if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
   }
@@ -395,7 +418,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
-                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.scale, sl2, n_qtiles);
+                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, n_qtiles);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -405,7 +428,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.scale, sl2, rows_pad);
+                     BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, rows_pad);
   timing_mark(a.stream, 3);
   return hipGetLastError();
 }

@@ -17,7 +17,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
-    float scale_log2, int n_qtiles) {
+    int window, float scale_log2, int n_qtiles) {
   constexpr int TPR = D / 32;          // lanes per query row
   constexpr int ROWS = 256 / TPR;      // query rows per workgroup
   constexpr int BC = 32;               // keys per LDS tile
@@ -46,12 +46,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     q[c] = x[0]; q[c + 1] = x[1]; q[c + 2] = x[2]; q[c + 3] = x[3];
     o[c] = o[c + 1] = o[c + 2] = o[c + 3] = 0.f;
   }
-  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;  // keys [0, row_limit)
+  // Keys [row_lo, row_limit); a sliding window of `window` keys (causal
+  // only, 0 = none) raises the lower end.
+  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
+  const int row_lo = (CAUSAL && window > 0) ? row + off - window + 1 : 0;
   const int last_row = min(qtile * ROWS + ROWS, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
+  const int kv_begin =
+      (CAUSAL && window > 0) ? max(0, qtile * ROWS + off - window + 1) / BC * BC : 0;
 
   float m = kNegInf, l = 0.f;
-  for (int k0 = 0; k0 < kv_end; k0 += BC) {
+  for (int k0 = kv_begin; k0 < kv_end; k0 += BC) {
     __syncthreads();
     for (int e = tid * 4; e < BC * D; e += 256 * 4) {
       const int r = e / D, c = e % D;
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int w = 1; w < TPR; w <<= 1) acc += __shfl_xor(acc, w);
-      const float x = (k0 + j < row_limit) ? acc * scale_log2 : kNegInf;
+      const float x = (k0 + j < row_limit && k0 + j >= row_lo) ? acc * scale_log2 : kNegInf;
       s[j] = x;
       mx = fmaxf(mx, x);
     }
@@ -150,7 +155,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
-    float scale_log2, int n_qtiles) {
+    int window, float scale_log2, int n_qtiles) {
   constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
   constexpr int BC = 32;         // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
@@ -186,7 +191,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const int last_row = min(q0 + BR, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  // Tiles before t_mask are fully visible to every row of the workgroup.
+  // A sliding window of `window` keys (causal only, 0 = none): row i sees
+  // keys [i + off - window + 1, i + off].  The loop starts at the first tile
+  // the workgroup's first row can see; tiles below t_lo cut some row's
+  // lower bound and are masked too.
+  const bool win = CAUSAL && window > 0;
+  const int j0 = win ? max(0, q0 + off - window + 1) / BC : 0;
+  const int t_lo = win ? max(0, last_row + off - window + 1 + BC - 1) / BC : 0;
+  // Tiles from t_mask on cut some row's causal bound.
   int t_mask = Skv / BC;
   if (CAUSAL) t_mask = min(t_mask, (q0 + off + 1) / BC);
 
@@ -201,8 +213,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
     qreg[c] ^= qsign;
   }
-  dma.load(Kh, Skv, sK0, 0, wave);
-  dma.load(Vh, Skv, sV0, 0, wave);
+  dma.load(Kh, Skv, sK0, j0 * BC, wave);
+  dma.load(Vh, Skv, sV0, j0 * BC, wave);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -210,7 +222,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [0, row_limit)
+  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [row_lo, row_limit)
+  const int row_lo = win ? row + off - window + 1 : 0;
 
   // Per-lane LDS byte offsets into the swizzled tiles.
   int k_off[kRowOffs<D>], v_off[kTrOffs<D>];
@@ -241,15 +254,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   };
-  // Scores of keys at or beyond the row's limit become -inf.
+  // Scores of keys outside [row_lo, row_limit) become -inf.
   auto mask = [&](f32x16* s, int k0) {
     const int lim = row_limit - k0 - 8 * g;
+    const int lo = row_lo - k0 - 8 * g;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = kb * 32 + 16 * (i >> 3) + (i & 7);
-        s[kb][i] = (kk < lim) ? s[kb][i] : kNegInf;
+        s[kb][i] = (kk < lim && kk >= lo) ? s[kb][i] : kNegInf;
       }
   };
   // One tile of the online softmax: advance the reference if the tile's
@@ -316,6 +330,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     // Tiles past the last key of this wave's rows are skipped.
     const int wave_kv_last =
         CAUSAL ? min(Skv, min(q0 + wave * 32 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
+    const int wave_kv_first = win ? q0 + wave * 32 + off - window + 1 : 0;
     f32x16 s[NKB];
     u32x4 p[NKB][2];
     auto step = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
@@ -325,9 +340,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       opaque_offsets<kTrOffs<D>>(v_off);
       dma.load(Kh, Skv, nK, (j + 1) * BC, wave);
       dma.load(Vh, Skv, nV, (j + 1) * BC, wave);
-      if (j * BC > wave_kv_last) return;
+      if (j * BC > wave_kv_last || j * BC + BC - 1 < wave_kv_first) return;
       qk(cK, s);
-      if (j >= t_mask) mask(s, j * BC);
+      if (j >= t_mask || j < t_lo) mask(s, j * BC);
       const float alpha = softmax(s, p);
       if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -338,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       pv(cV, p);
     };
 #pragma clang loop unroll(disable)
-    for (int j = 0; j < n_tiles; j += 2) {
+    for (int j = j0; j < n_tiles; j += 2) {
       step(j, sK0, sV0, sK1, sV1);
       if (j + 1 < n_tiles) step(j + 1, sK1, sV1, sK0, sV0);
     }
@@ -371,7 +386,7 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   timing_mark(a.stream, 0);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e, n_qtiles);
+                     BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
 }
@@ -391,8 +406,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   timing_mark(a.stream, 0);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3(n_qtiles * BH), dim3(64 * NW), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale * kLog2e,
-                     n_qtiles);
+                     (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window,
+                     a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, Hq, Hkv, Sq, Skv, d, causal;
+  int window;  // sliding-window width (causal only), 0 = none
   float scale;
   hipStream_t stream;
 };
@@ -54,6 +55,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   int B, Hq, Hkv, Sq, Skv, d, causal;
+  int window;  // sliding-window width (causal only), 0 = none
   float scale;
   float* ws;  // [B, Hq, Sqp] pairs (D = rowsum(dO * O), -LSE * log2(e)); Sqp = Sq rounded up to 32
   hipStream_t stream;

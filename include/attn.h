@@ -66,7 +66,8 @@ typedef enum {
   ATTN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
   ATTN_ERR_HIP = 7,         /* a HIP launch failed                              */
   ATTN_ERR_VALUE = 8        /* a scalar argument is invalid (scale not finite,
-                               n_splits out of range)                           */
+                               n_splits out of range, window without causal,
+                               page size not a multiple of 32)                  */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -92,11 +93,16 @@ int attn_supports(int dtype, int entry, int d);
  * Computed as the blockwise recurrence of the second display equation of
  * "Compilers and Kernels", FlashAttention section, one query tile per
  * workgroup.  Supported d: f32 {64, 128, 256}; bf16 {64, 128, 256}.
+ * Mask (the additive C of that section's first display equation):
+ *   causal != 0: key j allowed for query i iff j <= i + (Skv - Sq);
+ *   window > 0 (causal only, else ATTN_ERR_VALUE): also j > i + (Skv - Sq)
+ *   - window, a sliding window of `window` keys ending at the diagonal;
+ *   window <= 0: no window.
  */
 attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v,
                      void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Skv, int d,
-                     int causal, float scale, void* stream);
+                     int causal, int window, float scale, void* stream);
 
 /* Workspace for attn_decode: n_splits * B * Hq * (d + 2) float32 values,
  * rounded up to 256 bytes.  Returns 0 for invalid sizes. */
@@ -185,13 +191,14 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
  *   dq  [B, Hq, Sq, d], dk, dv [B, Hkv, Skv, d]   outputs, input dtype
  *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned; that
  *   size must stay below 4 GiB (else ATTN_ERR_SHAPE).
+ * causal and window as in attn_fwd (the same mask as the forward call).
  * Supported: bf16 with d in {64, 128}.
  */
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
                      const void* o, const void* d_o, const float* lse,
                      void* dq, void* dk, void* dv,
                      int B, int Hq, int Hkv, int Sq, int Skv, int d,
-                     int causal, float scale,
+                     int causal, int window, float scale,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert aos.attn_abi_version() == 1
+    assert aos.attn_abi_version() == 2
     for s in range(9):
         assert aos.attn_status_str(s) and aos.attn_status_str(s) != "unknown status"
     assert aos.attn_status_str(99) == "unknown status"
@@ -78,8 +78,9 @@ class Fake:
 
 
 def fwd(dt=BF16, q=1, k=1, v=1, o=1, lse=1, B=1, Hq=2, Hkv=1, Sq=8, Skv=8, d=64, causal=0,
-        scale=0.125):
-    return aos.lib().attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, scale, None)
+        scale=0.125, window=0):
+    return aos.lib().attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, window, scale,
+                              None)
 
 
 def test_fwd_validation():
@@ -91,6 +92,7 @@ def test_fwd_validation():
     assert fwd(**base, Sq=0) == SHAPE
     assert fwd(**base, Hq=3, Hkv=2) == SHAPE
     assert fwd(**base, Sq=9, Skv=8, causal=1) == SHAPE
+    assert fwd(**base, causal=0, window=4) == VALUE   # a window needs the causal mask
     assert fwd(**base, d=96) == UNSUP
     assert fwd(**base, dt=5) == UNSUP
     assert fwd(**base, scale=float("nan")) == VALUE
@@ -178,12 +180,12 @@ def test_bwd_validation():
 
     def call(**kw):
         a = dict(p)
-        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, scale=0.1,
-                      wsb=need))
+        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, window=0,
+                      scale=0.1, wsb=need))
         a.update(kw)
         return L.attn_bwd(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
                           a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["d"],
-                          a["causal"], a["scale"], a["ws"], a["wsb"], None)
+                          a["causal"], a["window"], a["scale"], a["ws"], a["wsb"], None)
 
     for n in names[:-1]:
         assert call(**{n: None}) == NULL, n
@@ -197,6 +199,7 @@ def test_bwd_validation():
     assert call(dq=p["do"]) == ALIAS
     assert call(ws=p["lse"]) == ALIAS
     assert call(dv=p["dv"] + 2) == ALIGN
+    assert call(causal=0, window=16) == VALUE        # a window needs the causal mask
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
