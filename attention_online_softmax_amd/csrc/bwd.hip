@@ -51,7 +51,7 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 // and Q^T come from transpose reads of the same tiles.  The loop covers the
 // query tiles of all query heads of the group.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   // Queries that can see any key of this tile: i >= first_key - off, and
   // with a sliding window of `window` keys (causal only, 0 = none) also
   // i < last_key - off + window.
-  const bool win = CAUSAL && window > 0;
+  const bool win = WIN;   // instantiated for causal calls with window > 0 only
   const int q_start = CAUSAL ? (max(0, ktile * 128 - off) / QT) * QT : 0;
   const int q_end = win ? min(Sq, ktile * 128 + 127 - off + window) : Sq;
   // Query tiles per head; 0 when no query's window reaches these keys
@@ -251,7 +251,7 @@ struct BwdTile {
 // lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
 // of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // Sliding window of `window` keys (causal only, 0 = none): row i sees
   // keys [i + off - window + 1, i + off]; the loop starts at the first tile
   // the workgroup's first row can see.
-  const bool win = CAUSAL && window > 0;
+  const bool win = WIN;   // instantiated for causal calls with window > 0 only
   const int t0 = win ? max(0, qtile * 128 + off - window + 1) / BC : 0;
 
   // K/V tiles through buffer loads; rows past Skv arrive as zeros (masked).
@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   store_transposed<NDB>(dQ + ((int64_t)bh * Sq + row) * D, dqt, g, scale);
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
+template <int D, bool CAUSAL, bool WIN>
+static hipError_t launch_bwd_w(const BwdArgs& a) {
   const int Sqp = (a.Sq + 31) / 32 * 32;
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
   const float sl2 = a.scale * kLog2e;
@@ -415,7 +415,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
                      BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, n_qtiles);
@@ -425,12 +425,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
   timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
                      BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, rows_pad);
   timing_mark(a.stream, 3);
   return hipGetLastError();
+}
+
+// The sliding window is a template parameter: calls without one run the
+// kernels with none of its index arithmetic.
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  if constexpr (CAUSAL) {
+    if (a.window > 0) return launch_bwd_w<D, true, true>(a);
+  }
+  return launch_bwd_w<D, CAUSAL, false>(a);
 }
 
 template <bool CAUSAL>

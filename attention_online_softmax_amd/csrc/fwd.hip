@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 constexpr float kLazy = 8.f;
 constexpr float kLazyBound = 256.f;   // 2^kLazy
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool WIN>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   // keys [i + off - window + 1, i + off].  The loop starts at the first tile
   // the workgroup's first row can see; tiles below t_lo cut some row's
   // lower bound and are masked too.
-  const bool win = CAUSAL && window > 0;
+  const bool win = WIN;   // instantiated for causal calls with window > 0 only
   const int j0 = win ? max(0, q0 + off - window + 1) / BC : 0;
   const int t_lo = win ? max(0, last_row + off - window + 1 + BC - 1) / BC : 0;
   // Tiles from t_mask on cut some row's causal bound.
@@ -398,18 +398,28 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
 template <int D>
 constexpr int kFwdWaves = D >= 256 ? 8 : 4;
 
-template <int D, bool CAUSAL>
-static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
+// The sliding window is a template parameter: calls without one run the
+// kernel with none of its index arithmetic.
+template <int D, bool CAUSAL, bool WIN>
+static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
   constexpr int NW = kFwdWaves<D>;
   const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3(n_qtiles * BH), dim3(64 * NW), 0,
-                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window,
-                     a.scale * kLog2e, n_qtiles);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN>), dim3(n_qtiles * BH), dim3(64 * NW),
+                     0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
+                     a.window, a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
+  if constexpr (CAUSAL) {
+    if (a.window > 0) return launch_fwd_bf16_w<D, true, true>(a);
+  }
+  return launch_fwd_bf16_w<D, CAUSAL, false>(a);
 }
 
 template <bool CAUSAL>
