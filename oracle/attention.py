@@ -27,6 +27,10 @@ Readings where the pages are silent (each is also listed in the design notes):
 * causal alignment for Sq != Skv is bottom-right: key j is allowed for query
   i iff j <= i + (Skv - Sq); causal with Sq > Skv would leave a row with no
   allowed key, which the definition excludes;
+* an additive bias is the mask C itself, given as a tensor: C[b, h, i, j]
+  (any real or -inf) is added to the scaled scores, on top of the causal and
+  window patterns; a row whose every key is -inf has O = 0 and LSE = -inf
+  (the definition asks for at least one allowed key per row);
 * a sliding window of W keys (W > 0, causal only) is one more pattern of the
   additive mask C: key j is allowed for query i iff
   i + (Skv - Sq) - W < j <= i + (Skv - Sq), so every row keeps its diagonal
@@ -106,18 +110,22 @@ def mask_matrix(rows, Sq, Skv, causal, window=0):
     return c
 
 
-def scores(q, k, causal, scale, b, hq, rows=None, window=0):
-    """S = Q K^T * scale + C for one (batch, query head), selected rows."""
+def scores(q, k, causal, scale, b, hq, rows=None, window=0, bias=None):
+    """S = Q K^T * scale + C for one (batch, query head), selected rows.
+    bias: optional [B, Hq, Sq, Skv] additive part of C (broadcast views of a
+    smaller array are fine)."""
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     g = Hq // Hkv
     if rows is None:
         rows = np.arange(Sq)
     s = (q[b, hq][rows] @ k[b, hq // g].T) * scale
+    if bias is not None:
+        s = s + bias[b, hq][rows]
     return s + mask_matrix(rows, Sq, Skv, causal, window)
 
 
-def attention_ref(q, k, v, causal, scale, rows=None, window=0):
+def attention_ref(q, k, v, causal, scale, rows=None, window=0, bias=None):
     """Scaled dot-product attention, the plain definition.
 
     Follows the first display equation of "Compilers and Kernels", section
@@ -128,7 +136,8 @@ def attention_ref(q, k, v, causal, scale, rows=None, window=0):
     rows: optional sorted array of query-row indices; when given, only those
     rows are computed and O is [B, Hq, len(rows), dv], LSE [B, Hq, len(rows)].
     window: sliding-window width W (causal only; <= 0: none).
-    Returns (O, LSE).
+    bias: optional additive mask values [B, Hq, Sq, Skv] (may hold -inf).
+    Returns (O, LSE); a row with no allowed key gets O = 0, LSE = -inf.
     """
     B, Hq, Hkv, Sq, Skv, d, dv = _check_shapes(q, k, v)
     if causal and Sq > Skv:
@@ -142,12 +151,17 @@ def attention_ref(q, k, v, causal, scale, rows=None, window=0):
             vv = v[b, h // g]
             for r0 in range(0, rows.size, _ROW_BLOCK):
                 rr = rows[r0:r0 + _ROW_BLOCK]
-                s = scores(q, k, causal, scale, b, h, rr, window)
+                s = scores(q, k, causal, scale, b, h, rr, window, bias)
                 m = s.max(axis=1)
-                e = np.exp(s - m[:, None])
+                live = m != NEG_INF
+                e = np.zeros_like(s)
+                e[live] = np.exp(s[live] - m[live][:, None])
                 l = e.sum(axis=1)
-                out[b, h, r0:r0 + rr.size] = (e @ vv) / l[:, None]
-                lse[b, h, r0:r0 + rr.size] = m + np.log(l)
+                o = np.zeros((rr.size, dv))
+                o[live] = (e[live] @ vv) / l[live][:, None]
+                out[b, h, r0:r0 + rr.size] = o
+                lse[b, h, r0:r0 + rr.size] = np.where(live, m + np.log(np.where(live, l, 1.0)),
+                                                      NEG_INF)
     return out, lse
 
 
@@ -389,7 +403,7 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, scale):
 # section: the backward recomputes local score and probability tiles).
 # ---------------------------------------------------------------------------
 
-def attention_bwd_ref(q, k, v, do, causal, scale, lse=None, window=0):
+def attention_bwd_ref(q, k, v, do, causal, scale, lse=None, window=0, bias=None):
     """Gradients of O = softmax(scale Q K^T + C) V with respect to Q, K, V.
 
     lse: [B, Hq, Sq] saved forward statistic; computed from the definition
@@ -400,7 +414,7 @@ def attention_bwd_ref(q, k, v, do, causal, scale, lse=None, window=0):
         raise ValueError("causal with Sq > Skv leaves a query row with no allowed key")
     g = Hq // Hkv
     if lse is None:
-        _, lse = attention_ref(q, k, v, causal, scale, window=window)
+        _, lse = attention_ref(q, k, v, causal, scale, window=window, bias=bias)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dvv = np.zeros_like(v)
@@ -408,8 +422,10 @@ def attention_bwd_ref(q, k, v, do, causal, scale, lse=None, window=0):
     for b in range(B):
         for h in range(Hq):
             kk, vv = k[b, h // g], v[b, h // g]
-            s = scores(q, k, causal, scale, b, h, window=window)
-            p = np.exp(s - lse[b, h][:, None])          # masked pairs: exp(-inf) = 0
+            s = scores(q, k, causal, scale, b, h, window=window, bias=bias)
+            live = lse[b, h] != NEG_INF                 # rows with at least one allowed key
+            p = np.zeros_like(s)
+            p[live] = np.exp(s[live] - lse[b, h][live][:, None])   # masked pairs: exp(-inf) = 0
             dp = do[b, h] @ vv.T
             D = (p * dp).sum(axis=1)
             ds = p * (dp - D[:, None])

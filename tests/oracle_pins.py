@@ -269,6 +269,72 @@ def pin_fwd_window(A):
         assert np.array_equal(O, Oc) and np.array_equal(L, Lc), "window >= Skv is causal"
 
 
+def pin_fwd_bias(A):
+    """Additive mask C given as a tensor: torch float64 sdpa with the same
+    float mask (alone and with the causal pattern), 50-digit brute force
+    with -inf entries, a constant per row (O unchanged, LSE shifted by it),
+    the causal pattern written as a 0 / -inf bias, broadcast batch / head
+    dimensions, and a row with every key masked (O = 0, LSE = -inf)."""
+    B, Hq, Hkv, Sq, Skv, d = 2, 4, 2, 9, 14, 8
+    q = _rand(70, B, Hq, Sq, d)
+    k = _rand(71, B, Hkv, Skv, d)
+    v = _rand(72, B, Hkv, Skv, d)
+    bias = _rand(73, B, Hq, Sq, Skv, mult=2.0)
+    scale = 1 / math.sqrt(d)
+    kt = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1)
+    causal_c = np.where(np.arange(Skv)[None, :] <= np.arange(Sq)[:, None] + (Skv - Sq), 0.0,
+                        -math.inf)
+    for causal in (False, True):
+        O, L = A.attention_ref(q, k, v, causal, scale, bias=bias)
+        mask = torch.from_numpy(bias + (causal_c if causal else 0.0))
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kt, vt,
+                                                               attn_mask=mask, scale=scale)
+        _close(O, ref.numpy(), 1e-13, f"bias sdpa O causal={causal}")
+    # brute force, -inf entries included
+    bq, bk, bv = q[:1, :2, :4, :3], k[:1, :1, :6, :3], v[:1, :1, :6, :3]
+    bb = bias[:1, :2, :4, :6].copy()
+    bb[0, 0, 1, 2] = bb[0, 1, 3, 0] = -math.inf
+    O, L = A.attention_ref(bq, bk, bv, False, 0.5, bias=bb)
+    mpmath.mp.dps = 50
+    for h in range(2):
+        for i in range(4):
+            es = [mpmath.mpf(0) if bb[0, h, i, j] == -math.inf else mpmath.exp(
+                mpmath.mpf(0.5) * mpmath.fsum(mpmath.mpf(bq[0, h, i, c]) * mpmath.mpf(bk[0, 0, j, c])
+                                              for c in range(3)) + mpmath.mpf(bb[0, h, i, j]))
+                  for j in range(6)]
+            den = mpmath.fsum(es)
+            for c in range(3):
+                _close(O[0, h, i, c], float(mpmath.fsum(e * mpmath.mpf(bv[0, 0, j, c])
+                                                         for j, e in enumerate(es)) / den),
+                       1e-13, "bias mpmath O")
+            _close(L[0, h, i], float(mpmath.log(den)), 1e-13, "bias mpmath LSE")
+    # a constant per row: softmax shift invariance
+    cst = _rand(74, B, Hq, Sq, 1, mult=5.0)
+    O0, L0 = A.attention_ref(q, k, v, True, scale)
+    O1, L1 = A.attention_ref(q, k, v, True, scale, bias=np.broadcast_to(cst, (B, Hq, Sq, Skv)))
+    _close(O1, O0, 1e-13, "constant bias O")
+    _close(L1, L0 + cst[..., 0], 1e-13, "constant bias LSE")
+    # the causal pattern as a bias; broadcast dimensions
+    Oc, Lc = A.attention_ref(q, k, v, False, scale,
+                             bias=np.broadcast_to(causal_c, (B, Hq, Sq, Skv)))
+    _close(Oc, O0, 1e-14, "causal as bias O")
+    _close(Lc, L0, 1e-14, "causal as bias LSE")
+    shared = bias[:1, :1]
+    Ob, Lb = A.attention_ref(q, k, v, True, scale, bias=np.broadcast_to(shared, bias.shape))
+    Oe, Le = A.attention_ref(q, k, v, True, scale, bias=np.repeat(np.repeat(shared, B, 0), Hq, 1))
+    assert np.array_equal(Ob, Oe) and np.array_equal(Lb, Le), "broadcast bias"
+    # a row with every key masked
+    dead = bias.copy()
+    dead[1, 2, 5, :] = -math.inf
+    O, L = A.attention_ref(q, k, v, False, scale, bias=dead)
+    assert np.all(O[1, 2, 5] == 0) and L[1, 2, 5] == -math.inf, "fully masked row"
+    Or, Lr = A.attention_ref(q, k, v, False, scale, bias=bias)
+    keep = np.ones((B, Hq, Sq), dtype=bool)
+    keep[1, 2, 5] = False
+    _close(O[keep], Or[keep], 0.0, "other rows unchanged")
+
+
 def pin_fwd_invariants(A):
     """Key shift moves LSE by scale q.u and keeps O; joint (K, V) row
     permutation keeps O (non-causal); grouped heads equal repeated heads."""
@@ -566,6 +632,26 @@ def pin_bwd_autograd(A):
         _close(dk, kt.grad.numpy(), 1e-12, "autograd dK")
         _close(dv, vt.grad.numpy(), 1e-12, "autograd dV")
         _close(D, np.sum(do * o.detach().numpy(), axis=-1), 1e-12, "D = rowsum(dO*O)")
+    # an additive bias tensor (with some -inf entries), with and without causal
+    bias = _rand(46, B, Hq, Sq, Skv, mult=1.5)
+    bias[0, 1, 3, :4] = -math.inf
+    for causal in (False, True):
+        qt = torch.from_numpy(q).requires_grad_()
+        kt = torch.from_numpy(k).requires_grad_()
+        vt = torch.from_numpy(v).requires_grad_()
+        kr = kt.repeat_interleave(Hq // Hkv, dim=1)
+        vr = vt.repeat_interleave(Hq // Hkv, dim=1)
+        s = (qt @ kr.transpose(-1, -2)) * scale + torch.from_numpy(bias)
+        if causal:
+            i = torch.arange(Sq)[:, None]
+            j = torch.arange(Skv)[None, :]
+            s = s.masked_fill(j > i + (Skv - Sq), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ vr
+        o.backward(torch.from_numpy(do))
+        dq, dk, dv, D = A.attention_bwd_ref(q, k, v, do, causal, scale, bias=bias)
+        _close(dq, qt.grad.numpy(), 1e-12, f"bias autograd dQ causal={causal}")
+        _close(dk, kt.grad.numpy(), 1e-12, f"bias autograd dK causal={causal}")
+        _close(dv, vt.grad.numpy(), 1e-12, f"bias autograd dV causal={causal}")
     # sliding windows (causal)
     i = torch.arange(Sq)[:, None]
     j = torch.arange(Skv)[None, :]
@@ -627,7 +713,7 @@ def pin_bwd_identities(A):
 
 FORWARD_PINS = [pin_fwd_mpmath, pin_fwd_golden, pin_fwd_uniform, pin_fwd_onehot,
                 pin_fwd_single_key, pin_fwd_scipy, pin_fwd_torch_sdpa, pin_fwd_window,
-                pin_fwd_invariants]
+                pin_fwd_bias, pin_fwd_invariants]
 MONOID_PINS = [pin_monoid_golden, pin_monoid_identity, pin_monoid_chunkings, pin_monoid_lse]
 DECODE_PINS = [pin_decode, pin_decode_paged]
 BACKWARD_PINS = [pin_bwd_finite_difference, pin_bwd_autograd, pin_bwd_golden, pin_bwd_identities]

@@ -26,12 +26,12 @@ MUTANTS = [
     ("GQA key head modulo", "k[b, hq // g].T", "k[b, hq % Hkv].T", 0),
     ("GQA value head modulo", "vv = v[b, h // g]\n            for r0",
      "vv = v[b, h % Hkv]\n            for r0", 0),
-    ("LSE without max", "lse[b, h, r0:r0 + rr.size] = m + np.log(l)",
-     "lse[b, h, r0:r0 + rr.size] = np.log(l)", 0),
-    ("O not normalised", "out[b, h, r0:r0 + rr.size] = (e @ vv) / l[:, None]",
-     "out[b, h, r0:r0 + rr.size] = (e @ vv)", 0),
-    ("O from keys", "out[b, h, r0:r0 + rr.size] = (e @ vv) / l[:, None]",
-     "out[b, h, r0:r0 + rr.size] = (e @ k[b, h // g]) / l[:, None]", 0),
+    ("LSE without max", "np.where(live, m + np.log(np.where(live, l, 1.0)),",
+     "np.where(live, np.log(np.where(live, l, 1.0)),", 0),
+    ("O not normalised", "o[live] = (e[live] @ vv) / l[live][:, None]",
+     "o[live] = (e[live] @ vv)", 0),
+    ("O from keys", "o[live] = (e[live] @ vv) / l[live][:, None]",
+     "o[live] = (e[live] @ k[b, h // g]) / l[live][:, None]", 0),
     ("merge weight sign", "w[live] = np.exp(m_from[live] - m_to[live])",
      "w[live] = np.exp(m_to[live] - m_from[live])", 0),
     ("merge drops a weight", "return m, wx * lx + wy * ly,", "return m, wx * lx + ly,", 0),
@@ -68,7 +68,13 @@ MUTANTS = [
     ("bwd dQ from values", "dq[b, h] = scale * (ds @ kk)", "dq[b, h] = scale * (ds @ vv)", 0),
     ("bwd D without P", "D = (p * dp).sum(axis=1)", "D = dp.sum(axis=1)", 0),
     ("bwd GQA overwrite", "dk[b, h // g] += scale", "dk[b, h // g] = scale", 0),
-    ("bwd P without LSE", "p = np.exp(s - lse[b, h][:, None])", "p = np.exp(s)", 0),
+    ("bwd P without LSE", "p[live] = np.exp(s[live] - lse[b, h][live][:, None])",
+     "p[live] = np.exp(s[live])", 0),
+    ("bias dropped", "        s = s + bias[b, hq][rows]", "        s = s + 0 * bias[b, hq][rows]", 0),
+    ("bias rows reversed", "        s = s + bias[b, hq][rows]",
+     "        s = s + bias[b, hq][::-1][rows]", 0),
+    ("bias by key head", "        s = s + bias[b, hq][rows]", "        s = s + bias[b, hq // g][rows]",
+     0),
 ]
 
 
