@@ -52,7 +52,8 @@ def lib():
     L.attn_supports.restype = i
     L.attn_supports.argtypes = [i, i, i]
     L.attn_fwd.restype = i
-    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    i64 = ctypes.c_int64
+    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, i64, i64, f, vp]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode.restype = i
@@ -64,7 +65,7 @@ def lib():
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_bwd.restype = i
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                           i, i, i, i, i, i, i, i, f, vp, sz, vp]
+                           i, i, i, i, i, i, i, i, vp, i64, i64, f, vp, sz, vp]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -132,10 +133,29 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _bias_args(bias, B, Hq, Sq, Skv, dev):
+    """(pointer, batch stride, head stride) of an additive fp32 bias that
+    broadcasts to [B, Hq, Sq, Skv] (size-1 batch / head dimensions broadcast;
+    the last two dimensions must be contiguous)."""
+    if bias is None:
+        return None, 0, 0
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.device != dev:
+        raise TypeError("bias must be a float32 tensor on the same GPU")
+    if bias.dim() != 4 or tuple(bias.shape[2:]) != (Sq, Skv) or bias.shape[0] not in (1, B) \
+            or bias.shape[1] not in (1, Hq):
+        raise ValueError("bias must broadcast to [B, Hq, Sq, Skv]")
+    if bias.stride(3) != 1 or bias.stride(2) != Skv:
+        raise ValueError("bias rows must be contiguous [Sq, Skv] planes")
+    sb = bias.stride(0) if bias.shape[0] == B and B > 1 else 0
+    sh = bias.stride(1) if bias.shape[1] == Hq and Hq > 1 else 0
+    return _ptr(bias), sb, sh
+
+
 def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, want_lse=True,
-             window=0):
+             window=0, bias=None):
     """Forward prefill.  q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d]; returns (o, lse).
-    window > 0 (with causal): a sliding window of that many keys."""
+    window > 0 (with causal): a sliding window of that many keys.
+    bias: optional fp32 additive mask broadcasting to [B, Hq, Sq, Skv]."""
     _check([q, k, v], ["q", "k", "v"])
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -147,7 +167,8 @@ def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None, w
         lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
     dt = _dtype_code(q)
     st = lib().attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                        B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), int(window), float(scale),
+                        B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), int(window),
+                        *_bias_args(bias, B, Hq, Sq, Skv, q.device), float(scale),
                         _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_fwd")
@@ -216,7 +237,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, n_
 
 
 def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, window=0):
+             workspace=None, stream=None, window=0, bias=None):
     """Backward (same causal / window as the forward call).  Returns (dq, dk, dv)."""
     _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
     B, Hq, Sq, d = q.shape
@@ -231,7 +252,8 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
         workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
     st = lib().attn_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                         _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
-                        int(bool(causal)), int(window), float(scale), _ptr(workspace),
+                        int(bool(causal)), int(window), *_bias_args(bias, B, Hq, Sq, Skv, q.device),
+                        float(scale), _ptr(workspace),
                         workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_bwd")

@@ -42,6 +42,20 @@ bool paged_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d =
 // Per-head element counts must stay within 32-bit index arithmetic.
 bool sizes_ok(int64_t S, int d) { return S * (int64_t)d < (int64_t(1) << 31); }
 
+// An additive bias: 16-byte aligned rows (Skv and both strides multiples
+// of 4 floats), non-negative strides; on success *extent is its byte span.
+attn_status check_bias(const float* bias, int64_t sb, int64_t sh, int B, int Hq, int Sq, int Skv,
+                       int64_t* extent) {
+  *extent = 0;
+  if (!bias) return ATTN_OK;
+  if (sb < 0 || sh < 0) return ATTN_ERR_VALUE;
+  if (!aligned16(bias) || Skv % 4 != 0 || sb % 4 != 0 || sh % 4 != 0) return ATTN_ERR_ALIGN;
+  const int64_t last = (int64_t)(B - 1) * sb + (int64_t)(Hq - 1) * sh + (int64_t)Sq * Skv;
+  if (last >= (int64_t(1) << 60) / 4) return ATTN_ERR_SHAPE;
+  *extent = last * 4;
+  return ATTN_OK;
+}
+
 // Outputs must not overlap inputs or each other.
 attn_status check_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
   for (int i = 0; i < n_out; ++i) {
@@ -108,7 +122,8 @@ int attn_supports(int dtype, int entry, int d) {
 
 attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
-                     float scale, void* stream) {
+                     const float* bias, int64_t bias_sb, int64_t bias_sh, float scale,
+                     void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -116,18 +131,23 @@ attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
   if (window > 0 && !causal) return ATTN_ERR_VALUE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   if (!fwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  // bf16 with a bias: d <= 128 (the d256 kernel has no registers to spare).
+  if (bias && dtype == ATTN_BF16 && d > 128) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  int64_t bias_bytes = 0;
+  attn_status st = check_bias(bias, bias_sb, bias_sh, B, Hq, Sq, Skv, &bias_bytes);
+  if (st != ATTN_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_ALIGN;
   const int es = esize(dtype);
-  const Span ins[3] = {span(q, (int64_t)B * Hq * Sq * d * es), span(k, (int64_t)B * Hkv * Skv * d * es),
-                       span(v, (int64_t)B * Hkv * Skv * d * es)};
+  const Span ins[4] = {span(q, (int64_t)B * Hq * Sq * d * es), span(k, (int64_t)B * Hkv * Skv * d * es),
+                       span(v, (int64_t)B * Hkv * Skv * d * es), span(bias, bias_bytes)};
   const Span outs[2] = {span(o, (int64_t)B * Hq * Sq * d * es),
                         lse ? span(lse, (int64_t)B * Hq * Sq * 4) : Span{0, 0}};
-  attn_status st = check_alias(outs, 2, ins, 3);
+  st = check_alias(outs, 2, ins, 4);
   if (st != ATTN_OK) return st;
   attn::FwdArgs a{dtype, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0,
-                  window > 0 ? window : 0, scale, (hipStream_t)stream};
+                  window > 0 ? window : 0, bias, bias_sb, bias_sh, scale, (hipStream_t)stream};
   return hip_status(attn::launch_fwd(a));
 }
 
@@ -213,7 +233,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d) {
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
                      const void* d_o, const float* lse, void* dq, void* dk, void* dv, int B,
                      int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
-                     float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                     const float* bias, int64_t bias_sb, int64_t bias_sh, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -224,6 +245,9 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
   if (!bwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  int64_t bias_bytes = 0;
+  attn_status st = check_bias(bias, bias_sb, bias_sh, B, Hq, Sq, Skv, &bias_bytes);
+  if (st != ATTN_OK) return st;
   if (!workspace) return ATTN_ERR_WORKSPACE;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Sq, d)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
@@ -231,15 +255,15 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
     return ATTN_ERR_ALIGN;
   const int es = esize(dtype);
   const int64_t nq = (int64_t)B * Hq * Sq * d * es, nkv = (int64_t)B * Hkv * Skv * d * es;
-  const Span ins[6] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
-                       span(lse, (int64_t)B * Hq * Sq * 4)};
+  const Span ins[7] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
+                       span(lse, (int64_t)B * Hq * Sq * 4), span(bias, bias_bytes)};
   const Span outs[4] = {span(dq, nq), span(dk, nkv), span(dv, nkv),
                         span(workspace, (int64_t)attn_bwd_workspace_bytes(B, Hq, Sq, d))};
-  attn_status st = check_alias(outs, 4, ins, 6);
+  st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
   attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
-                  causal ? 1 : 0, window > 0 ? window : 0, scale, (float*)workspace,
-                  (hipStream_t)stream};
+                  causal ? 1 : 0, window > 0 ? window : 0, bias, bias_sb, bias_sh, scale,
+                  (float*)workspace, (hipStream_t)stream};
   return hip_status(attn::launch_bwd(a));
 }
 

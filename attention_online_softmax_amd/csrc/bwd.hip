@@ -51,12 +51,13 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 // and Q^T come from transpose reads of the same tiles.  The loop covers the
 // query tiles of all query heads of the group.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
-    float scale, float scale_log2, int64_t rows_pad) {
+    const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale, float scale_log2,
+    int64_t rows_pad) {
   constexpr int QT = 32;   // query rows per tile
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -149,10 +150,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   // i%8 of the tile, key `key`); P = exp(scale S - LSE), dS = P (dP - D);
   // dV^T += dO^T P, dK^T += Q^T dS.  Only the softmax step is inside the
   // mask branch; the accumulators are updated outside it.
-  auto step = [&](const uint16_t* slot, int qs) {
+  // Additive bias of this lane's key for the tile's queries (element (c, j)
+  // is query qs + 16c + 8g + j), requested before the products that precede
+  // its use.
+  const int bkey = min(key, Skv - 1);
+  auto load_bias = [&](int qs, int hh, float* bv) {
+    const float* bp = bias + b * bsb + (int64_t)(hk * G + hh) * bsh + bkey;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      bv[i] = bp[(int64_t)min(qs + 16 * (i >> 3) + 8 * g + (i & 7), Sq - 1) * Skv];
+  };
+  auto step = [&](const uint16_t* slot, int qs, int hh) {
     const uint16_t* cQ = slot;
     const uint16_t* cG = slot + QT * D;
     const float* cN = (const float*)(slot + 2 * QT * D);
+    float bv[16];
+    if constexpr (BIAS) load_bias(qs, hh, bv);
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
           const int i = 8 * c + j;
           const float dd = dn[j >> 1][2 * (j & 1)];
           const float nl = dn[j >> 1][2 * (j & 1) + 1];
-          float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+          float p = fast_exp2(fmaf(s[i], scale_log2, BIAS ? fmaf(bv[i], kLog2e, nl) : nl));
           if constexpr (decltype(msk)::value) p = (16 * c + j >= lo && 16 * c + j <= hi) ? p : 0.f;
           pv[j] = p;
           dsv[j] = p * (dp[i] - dd);
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     }
   };
 
-  int cur_qt = 0;   // query tile of the next step
+  int cur_qt = 0, cur_hh = 0;   // query tile and query head of the next step
   auto body = [&](const uint16_t* cur, uint16_t* nxt) {
     wait_vmcnt0();   // this wave's part of the current tile (and V) has landed
     lds_barrier();   // ... and every wave's; the other slot is no longer read
@@ -215,12 +228,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     opaque_offsets<kTrOffs<D>>(t_off);
     issue(nxt);
     const int qs = q_start + cur_qt * QT;
-    if (++cur_qt == n_qt) cur_qt = 0;
+    const int hh = cur_hh;
+    if (++cur_qt == n_qt) {
+      cur_qt = 0;
+      ++cur_hh;
+    }
     // Tiles whose queries all precede this wave's first visible key, or
     // whose windows all start after its last key: skip.
     if (CAUSAL && qs + QT - 1 + off < key0_wave) return;
     if (win && qs + off - window + 1 > key0_wave + 31) return;
-    step(cur, qs);
+    step(cur, qs, hh);
   };
 #pragma clang loop unroll(disable)
   for (int i = 0; i < n_it; i += 2) {
@@ -251,13 +268,13 @@ struct BwdTile {
 // lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
 // of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
     const float* __restrict__ LSE, float* __restrict__ ws, uint16_t* __restrict__ dQ, int BH,
-    int Hq, int Hkv, int Sq, int Sqp, int Skv, int window, float scale, float scale_log2,
-    int n_qtiles) {
+    int Hq, int Hkv, int Sq, int Sqp, int Skv, int window, const float* __restrict__ bias,
+    int64_t bsb, int64_t bsh, float scale, float scale_log2, int n_qtiles) {
   constexpr int BC = BwdTile<D>::KB;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -320,7 +337,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
   dacc = halfwave_sum(dacc);
   const float dd = valid ? dacc : 0.f;
-  const float nl = valid ? -LSE[(int64_t)bh * Sq + qrow] * kLog2e : kNegInf;
+  // A row with no allowed key (LSE = -inf, possible with a bias) gets
+  // probabilities 0, like the padding rows.
+  const float lse_row = valid ? LSE[(int64_t)bh * Sq + qrow] : kNegInf;
+  const float nl = lse_row != kNegInf ? -lse_row * kLog2e : kNegInf;
   if (g == 0 && row < Sqp) *(f32x2*)(ws + 2 * ((int64_t)bh * Sqp + row)) = f32x2{dd, nl};
   f32x16 dqt[NDB];
 #pragma unroll
@@ -330,6 +350,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;   // keys [row_lo, row_limit)
   const int row_lo = win ? row + off - window + 1 : 0;
+  const float* brow = BIAS ? bias + b * bsb + h * bsh + (int64_t)qrow * Skv : nullptr;
   const int wave_kv_last = CAUSAL ? min(Skv, min(wave_row0 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
   const int wave_kv_first = win ? wave_row0 + off - window + 1 : 0;
   const int wave_lo_max = win ? min(wave_row0 + 31, Sq - 1) + off - window + 1 : 0;
@@ -353,6 +374,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       if (ks > wave_kv_last || ks + 31 < wave_kv_first) continue;
       const bool need_mask = (ks + 32 > Skv) || (CAUSAL && ks + 31 > wave_row0 + off) ||
                              (win && ks < wave_lo_max);
+      // Additive bias of this lane's query for keys ks + 16c + 8g + 0..7
+      // (bv[2c], bv[2c + 1]), requested before the products.
+      f32x4 bv[4];
+      if constexpr (BIAS) {
+        if (ks + 32 <= Skv) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bv[e] = *(const f32x4*)(brow + ks + 16 * (e >> 1) + 8 * g + 4 * (e & 1));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              bv[e][x] = brow[min(ks + 16 * (e >> 1) + 8 * g + 4 * (e & 1) + x, Skv - 1)];
+        }
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
@@ -375,7 +412,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const int i = 8 * c + 2 * j + u;
-              float p = fast_exp2(fmaf(s[i], scale_log2, nl));
+              const float pre =
+                  BIAS ? fmaf(bv[2 * c + (j >> 1)][2 * (j & 1) + u], kLog2e, nl) : nl;
+              float p = fast_exp2(fmaf(s[i], scale_log2, pre));
               if constexpr (decltype(masked)::value) {
                 const int kk = ks + 16 * c + 8 * g + 2 * j + u;
                 p = (kk < row_limit && kk >= row_lo) ? p : 0.f;
@@ -406,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   store_transposed<NDB>(dQ + ((int64_t)bh * Sq + row) * D, dqt, g, scale);
 }
 
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 static hipError_t launch_bwd_w(const BwdArgs& a) {
   const int Sqp = (a.Sq + 31) / 32 * 32;
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
@@ -415,32 +454,40 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
-                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, n_qtiles);
+                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
+                     a.scale, sl2, n_qtiles);
   timing_mark(a.stream, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
   timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.scale, sl2, rows_pad);
+                     BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb,
+                     a.bias_sh, a.scale, sl2, rows_pad);
   timing_mark(a.stream, 3);
   return hipGetLastError();
 }
 
-// The sliding window is a template parameter: calls without one run the
-// kernels with none of its index arithmetic.
+// The sliding window and the additive bias are template parameters: calls
+// without them run the kernels with none of their arithmetic.
+template <int D, bool CAUSAL, bool WIN>
+static hipError_t launch_bwd_b(const BwdArgs& a) {
+  if (a.bias) return launch_bwd_w<D, CAUSAL, WIN, true>(a);
+  return launch_bwd_w<D, CAUSAL, WIN, false>(a);
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   if constexpr (CAUSAL) {
-    if (a.window > 0) return launch_bwd_w<D, true, true>(a);
+    if (a.window > 0) return launch_bwd_b<D, true, true>(a);
   }
-  return launch_bwd_w<D, CAUSAL, false>(a);
+  return launch_bwd_b<D, CAUSAL, false>(a);
 }
 
 template <bool CAUSAL>

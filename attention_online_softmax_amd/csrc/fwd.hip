@@ -17,7 +17,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
-    int window, float scale_log2, int n_qtiles) {
+    int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
+    int n_qtiles) {
   constexpr int TPR = D / 32;          // lanes per query row
   constexpr int ROWS = 256 / TPR;      // query rows per workgroup
   constexpr int BC = 32;               // keys per LDS tile
@@ -54,6 +55,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int kv_begin =
       (CAUSAL && window > 0) ? max(0, qtile * ROWS + off - window + 1) / BC * BC : 0;
+  // Additive bias row of this query (row i of the [Sq, Skv] bias plane).
+  const float* brow =
+      bias ? bias + b * bsb + h * bsh + (int64_t)min(row, Sq - 1) * Skv : nullptr;
 
   float m = kNegInf, l = 0.f;
   for (int k0 = kv_begin; k0 < kv_end; k0 += BC) {
@@ -86,7 +90,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int w = 1; w < TPR; w <<= 1) acc += __shfl_xor(acc, w);
-      const float x = (k0 + j < row_limit && k0 + j >= row_lo) ? acc * scale_log2 : kNegInf;
+      float x = kNegInf;
+      if (k0 + j < row_limit && k0 + j >= row_lo)
+        x = brow ? fmaf(brow[k0 + j], kLog2e, acc * scale_log2) : acc * scale_log2;
       s[j] = x;
       mx = fmaxf(mx, x);
     }
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     m = mx;
   }
   if (!valid) return;
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   float* Oh = O + ((int64_t)bh * Sq + row) * D + col0;
 #pragma unroll
   for (int c = 0; c < 32; c += 4) {
@@ -151,11 +157,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 constexpr float kLazy = 8.f;
 constexpr float kLazyBound = 256.f;   // 2^kLazy
 
-template <int D, bool CAUSAL, int NW, bool WIN>
+template <int D, bool CAUSAL, int NW, bool WIN, bool BIAS>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
-    int window, float scale_log2, int n_qtiles) {
+    int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
+    int n_qtiles) {
   constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
   constexpr int BC = 32;         // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
@@ -206,6 +213,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   // so the maximum can be taken on raw scores and scaled afterwards.
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float c2 = fabsf(scale_log2);
+  // With an additive bias the scores are taken to the log2 domain before the
+  // softmax (s c2 + bias log2(e)), which then works with unit scale.
+  const float c2s = BIAS ? 1.f : c2;
   u32x4 qreg[NDC];
   const int qrow = min(row, Sq - 1);
 #pragma unroll
@@ -284,8 +294,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2, -msub));
-            const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2, -msub));
+            const float p0 = fast_exp2(fmaf(s[kb][8 * c + 2 * j], c2s, -msub));
+            const float p1 = fast_exp2(fmaf(s[kb][8 * c + 2 * j + 1], c2s, -msub));
             sum += p0 + p1;
             pb[kb][c][j] = pack_bf16x2(p0, p1);
           }
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[kb][i]);
-      const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
+      const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2s);
       alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
       m_ref = mnew;
       lsum = exps((m_ref == kNegInf) ? 0.f : m_ref);
@@ -331,6 +341,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const int wave_kv_last =
         CAUSAL ? min(Skv, min(q0 + wave * 32 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
     const int wave_kv_first = win ? q0 + wave * 32 + off - window + 1 : 0;
+    // Additive bias of this lane's query for the keys it holds: keys
+    // k0 + 16c + 8g + 0..7 (c = 0, 1) in bv[2c], bv[2c + 1].  The next
+    // tile's values are requested while the current tile is used.
+    const float* brow =
+        BIAS ? bias + b * bsb + h * bsh + (int64_t)min(row, Sq - 1) * Skv : nullptr;
+    auto load_bias = [&](int k0, f32x4* bv) {
+      if (k0 + BC <= Skv) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = *(const f32x4*)(brow + k0 + 16 * (e >> 1) + 8 * g + 4 * (e & 1));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            bv[e][x] = brow[min(k0 + 16 * (e >> 1) + 8 * g + 4 * (e & 1) + x, Skv - 1)];
+      }
+    };
+    f32x4 bnext[4];
+    if constexpr (BIAS) load_bias(j0 * BC, bnext);
     f32x16 s[NKB];
     u32x4 p[NKB][2];
     auto step = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
@@ -340,8 +369,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       opaque_offsets<kTrOffs<D>>(v_off);
       dma.load(Kh, Skv, nK, (j + 1) * BC, wave);
       dma.load(Vh, Skv, nV, (j + 1) * BC, wave);
+      f32x4 bcur[4];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bcur[e] = bnext[e];
+        if (j + 1 < n_tiles) load_bias((j + 1) * BC, bnext);
+      }
       if (j * BC > wave_kv_last || j * BC + BC - 1 < wave_kv_first) return;
       qk(cK, s);
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[0][i] = fmaf(s[0][i], c2, bcur[2 * (i >> 3) + ((i & 7) >> 2)][i & 3] * kLog2e);
+      }
       if (j >= t_mask || j < t_lo) mask(s, j * BC);
       const float alpha = softmax(s, p);
       if (__any(alpha != 1.f)) {
@@ -361,7 +401,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
   const float l = halfwave_sum(lpart);
   if (!valid) return;
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   uint16_t* Orow = O + ((int64_t)bh * Sq + row) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -386,7 +426,8 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   timing_mark(a.stream, 0);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.scale * kLog2e, n_qtiles);
+                     BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
+                     a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
 }
@@ -400,26 +441,38 @@ constexpr int kFwdWaves = D >= 256 ? 8 : 4;
 
 // The sliding window is a template parameter: calls without one run the
 // kernel with none of its index arithmetic.
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
   constexpr int NW = kFwdWaves<D>;
   const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN>), dim3(n_qtiles * BH), dim3(64 * NW),
-                     0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN, BIAS>), dim3(n_qtiles * BH),
+                     dim3(64 * NW), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
-                     a.window, a.scale * kLog2e, n_qtiles);
+                     a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
+}
+
+// An additive bias is a template parameter too (d <= 128: the d256 kernel
+// has no registers to spare for the bias of its tiles).
+template <int D, bool CAUSAL, bool WIN>
+static hipError_t launch_fwd_bf16_b(const FwdArgs& a) {
+  if constexpr (D <= 128) {
+    if (a.bias) return launch_fwd_bf16_w<D, CAUSAL, WIN, true>(a);
+  } else {
+    if (a.bias) return hipErrorInvalidValue;
+  }
+  return launch_fwd_bf16_w<D, CAUSAL, WIN, false>(a);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   if constexpr (CAUSAL) {
-    if (a.window > 0) return launch_fwd_bf16_w<D, true, true>(a);
+    if (a.window > 0) return launch_fwd_bf16_b<D, true, true>(a);
   }
-  return launch_fwd_bf16_w<D, CAUSAL, false>(a);
+  return launch_fwd_bf16_b<D, CAUSAL, false>(a);
 }
 
 template <bool CAUSAL>

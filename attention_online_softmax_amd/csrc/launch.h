@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace attn {
 
@@ -16,6 +17,8 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, Sq, Skv, d, causal;
   int window;  // sliding-window width (causal only), 0 = none
+  const float* bias;  // additive mask bias[b*bias_sb + h*bias_sh + i*Skv + j], or nullptr
+  int64_t bias_sb, bias_sh;
   float scale;
   hipStream_t stream;
 };
@@ -56,6 +59,8 @@ struct BwdArgs {
   void* dv;
   int B, Hq, Hkv, Sq, Skv, d, causal;
   int window;  // sliding-window width (causal only), 0 = none
+  const float* bias;  // as in FwdArgs
+  int64_t bias_sb, bias_sh;
   float scale;
   float* ws;  // [B, Hq, Sqp] pairs (D = rowsum(dO * O), -LSE * log2(e)); Sqp = Sq rounded up to 32
   hipStream_t stream;

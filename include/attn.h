@@ -50,6 +50,7 @@
 #define ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -97,12 +98,20 @@ int attn_supports(int dtype, int entry, int d);
  *   causal != 0: key j allowed for query i iff j <= i + (Skv - Sq);
  *   window > 0 (causal only, else ATTN_ERR_VALUE): also j > i + (Skv - Sq)
  *   - window, a sliding window of `window` keys ending at the diagonal;
- *   window <= 0: no window.
+ *   window <= 0: no window;
+ *   bias (may be NULL): float32 values added to the scaled scores,
+ *   bias[b * bias_sb + h * bias_sh + i * Skv + j] for query head h (strides
+ *   in elements, 0 to broadcast over batch or heads), any real or -inf; the
+ *   pointer 16-byte aligned and Skv, bias_sb, bias_sh multiples of 4 (else
+ *   ATTN_ERR_ALIGN), strides >= 0 (else ATTN_ERR_VALUE); bf16 with a bias
+ *   supports d in {64, 128} (else ATTN_ERR_UNSUPPORTED).  A row whose every
+ *   key is masked gets O = 0 and lse = -inf.
  */
 attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v,
                      void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Skv, int d,
-                     int causal, int window, float scale, void* stream);
+                     int causal, int window, const float* bias, int64_t bias_sb,
+                     int64_t bias_sh, float scale, void* stream);
 
 /* Workspace for attn_decode: n_splits * B * Hq * (d + 2) float32 values,
  * rounded up to 256 bytes.  Returns 0 for invalid sizes. */
@@ -191,14 +200,17 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
  *   dq  [B, Hq, Sq, d], dk, dv [B, Hkv, Skv, d]   outputs, input dtype
  *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned; that
  *   size must stay below 4 GiB (else ATTN_ERR_SHAPE).
- * causal and window as in attn_fwd (the same mask as the forward call).
+ * causal, window and bias as in attn_fwd (the same mask as the forward
+ * call; no gradient is formed for the bias).  Rows with lse = -inf (no
+ * allowed key) contribute nothing.
  * Supported: bf16 with d in {64, 128}.
  */
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
                      const void* o, const void* d_o, const float* lse,
                      void* dq, void* dk, void* dv,
                      int B, int Hq, int Hkv, int Sq, int Skv, int d,
-                     int causal, int window, float scale,
+                     int causal, int window, const float* bias, int64_t bias_sb,
+                     int64_t bias_sh, float scale,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*

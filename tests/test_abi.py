@@ -78,9 +78,9 @@ class Fake:
 
 
 def fwd(dt=BF16, q=1, k=1, v=1, o=1, lse=1, B=1, Hq=2, Hkv=1, Sq=8, Skv=8, d=64, causal=0,
-        scale=0.125, window=0):
-    return aos.lib().attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, window, scale,
-                              None)
+        scale=0.125, window=0, bias=None, sb=0, sh=0):
+    return aos.lib().attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, window, bias,
+                              sb, sh, scale, None)
 
 
 def test_fwd_validation():
@@ -93,6 +93,13 @@ def test_fwd_validation():
     assert fwd(**base, Hq=3, Hkv=2) == SHAPE
     assert fwd(**base, Sq=9, Skv=8, causal=1) == SHAPE
     assert fwd(**base, causal=0, window=4) == VALUE   # a window needs the causal mask
+    bias = f()
+    assert fwd(**base, bias=bias, Skv=6, Sq=6) == ALIGN     # rows of 6 floats: not 16-byte aligned
+    assert fwd(**base, bias=bias + 4) == ALIGN
+    assert fwd(**base, bias=bias, sb=6) == ALIGN
+    assert fwd(**base, bias=bias, sh=-4) == VALUE
+    assert fwd(**dict(base, d=256), bias=bias) == UNSUP      # bf16 d256 takes no bias
+    assert fwd(**base, bias=p["o"]) == ALIAS                 # the bias overlaps an output
     assert fwd(**base, d=96) == UNSUP
     assert fwd(**base, dt=5) == UNSUP
     assert fwd(**base, scale=float("nan")) == VALUE
@@ -181,11 +188,12 @@ def test_bwd_validation():
     def call(**kw):
         a = dict(p)
         a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, window=0,
-                      scale=0.1, wsb=need))
+                      bias=None, sb=0, sh=0, scale=0.1, wsb=need))
         a.update(kw)
         return L.attn_bwd(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
                           a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["d"],
-                          a["causal"], a["window"], a["scale"], a["ws"], a["wsb"], None)
+                          a["causal"], a["window"], a["bias"], a["sb"], a["sh"], a["scale"],
+                          a["ws"], a["wsb"], None)
 
     for n in names[:-1]:
         assert call(**{n: None}) == NULL, n
@@ -200,6 +208,9 @@ def test_bwd_validation():
     assert call(ws=p["lse"]) == ALIAS
     assert call(dv=p["dv"] + 2) == ALIGN
     assert call(causal=0, window=16) == VALUE        # a window needs the causal mask
+    assert call(bias=p["ws"]) == ALIAS               # the bias overlaps the workspace
+    assert call(bias=f() + 8) == ALIGN
+    assert call(bias=f(), sb=-8) == VALUE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
