@@ -5,7 +5,8 @@ One step = attn_fwd followed by attn_bwd on the training workload
 split-KV decode, which is timed in the same run on its own workload
 (bf16, B=8, Hq=32, Hkv=8, Skv=4096, d=128, 16 splits), as are the same
 decode over a paged cache (shuffled 64-key pages), the training step with
-a 512-key sliding window and the 44k-token head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
+a 512-key sliding window, the training step with an additive fp32 bias, and
+the 44k-token head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
 resident in device memory; three input sets rotate so that no step reuses
 the previous step's data from the 256 MiB last-level cache.
 
@@ -389,16 +390,20 @@ def bench_decode_paged(args, hev, stream, reps):
             "algorithmic_bytes": algo}
 
 
-def bench_window(args, hev, stream, reps, window=512):
+def bench_masked(args, hev, stream, reps, window=0, with_bias=False):
     """Forward + backward of the training shape (B4 H16 S2048 d128, causal)
-    with a sliding window of `window` keys; algorithmic FLOPs count the
-    allowed pairs of the window only (4 d per pair forward, 10 d backward)."""
+    with a sliding window of `window` keys and/or an additive fp32 bias
+    shared by all batches and heads ([1, 1, S, S], N(0, 1) values).
+    Algorithmic FLOPs count the allowed pairs only (4 d per pair forward,
+    10 d backward)."""
     import torch
     import attention_online_softmax_amd as aos
-    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload, randn
     w = WORKLOADS["train_fwd_bwd"]
     sets = [{k: v.cuda() for k, v in make_workload(w, w.seed_base + 100 * i).items()}
             for i in range(3)]
+    bias = (randn((1, 1, w.Sq, w.Skv), w.seed_base + 7, 1.0, torch.float32).cuda()
+            if with_bias else None)
     outs = []
     for s in sets:
         outs.append(dict(o=torch.empty_like(s["q"]),
@@ -411,12 +416,13 @@ def bench_window(args, hev, stream, reps, window=512):
     def fwd(i):
         s, o = sets[i % 3], outs[i % 3]
         aos.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w.scale, o=o["o"], lse=o["lse"],
-                     window=window)
+                     window=window, bias=bias)
 
     def bwd(i):
         s, o = sets[i % 3], outs[i % 3]
         aos.attn_bwd(s["q"], s["k"], s["v"], o["o"], s["do"], o["lse"], causal=True, scale=w.scale,
-                     dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["ws"], window=window)
+                     dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["ws"], window=window,
+                     bias=bias)
 
     for i in range(3):
         fwd(i)
@@ -425,12 +431,15 @@ def bench_window(args, hev, stream, reps, window=512):
     total_ms, _, spans = run_calls([("fwd", fwd), ("bwd", bwd)], {"fwd": 1, "bwd": 2}, hev, reps,
                                    stream, slots={"fwd": {0, 1}, "bwd": {0, 3}})
     off = w.Skv - w.Sq
-    pairs = sum(min(i + off + 1, w.Skv) - max(0, i + off - window + 1) for i in range(w.Sq))
+    lo = (lambda i: max(0, i + off - window + 1)) if window > 0 else (lambda i: 0)
+    pairs = sum(min(i + off + 1, w.Skv) - lo(i) for i in range(w.Sq))
     flop_fwd = 4.0 * w.d * pairs * w.B * w.Hq
     fq = quantiles([t for t in spans["fwd"] if t is not None])
     bq = quantiles([t for t in spans["bwd"] if t is not None])
     ms = total_ms / reps
-    return {"workload": f"window_fwd_bwd: bf16 causal B4 H16 S2048 d128, window {window}",
+    what = ", ".join(x for x in (f"window {window}" if window > 0 else "",
+                                 "shared fp32 bias [1,1,S,S]" if with_bias else "") if x)
+    return {"workload": f"train shape bf16 causal B4 H16 S2048 d128, {what}",
             "ms_per_step": ms, "TFLOP/s": 3.5 * flop_fwd / (ms * 1e-3) / 1e12,
             "fwd_ms": fq["median"], "fwd_TFLOP/s": flop_fwd / (fq["median"] * 1e-3) / 1e12,
             "bwd_ms": bq["median"], "bwd_TFLOP/s": 2.5 * flop_fwd / (bq["median"] * 1e-3) / 1e12,
@@ -560,8 +569,12 @@ def main():
         extras["paged_decode"] = bench_decode_paged(args, hev, stream, max(args.steps, 50))
         print(f"[bench] paged decode: {extras['paged_decode']['us_median']:.1f} us",
               file=sys.stderr, flush=True)
-        extras["window_fwd_bwd"] = bench_window(args, hev, stream, max(args.steps, 20))
+        extras["window_fwd_bwd"] = bench_masked(args, hev, stream, max(args.steps, 20), window=512)
         print(f"[bench] window 512 fwd+bwd: {extras['window_fwd_bwd']['ms_per_step']:.3f} ms/step",
+              file=sys.stderr, flush=True)
+        extras["bias_fwd_bwd"] = bench_masked(args, hev, stream, max(args.steps, 20),
+                                              with_bias=True)
+        print(f"[bench] bias fwd+bwd: {extras['bias_fwd_bwd']['ms_per_step']:.3f} ms/step",
               file=sys.stderr, flush=True)
         extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
         print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",
