@@ -24,6 +24,8 @@ FWD_CASES = [
     (1, 2, 2, 150, 150, 64, 33, "f32"),
     (1, 1, 1, 90, 200, 128, 17, "f32"),
     (1, 2, 2, 70, 70, 256, 5, "f32"),
+    (1, 2, 1, 1, 100, 128, 10, "bf16"),
+    (1, 2, 2, 5, 300, 64, 7, "f32"),
 ]
 
 # (B, Hq, Hkv, Sq, Skv, d, window)
@@ -33,6 +35,7 @@ BWD_CASES = [
     (1, 8, 1, 300, 300, 128, 1),
     (1, 2, 2, 160, 160, 128, 1000),
     (1, 2, 1, 97, 161, 64, 40),
+    (1, 2, 1, 3, 200, 64, 16),
 ]
 
 
