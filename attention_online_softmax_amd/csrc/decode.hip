@@ -1,13 +1,16 @@
 // Split-KV decode: one query token per (batch, query head) against a long
-// contiguous KV cache.  The keys are cut into contiguous chunks; each chunk's
+// KV cache (contiguous, or paged through a block table).  The keys are
+// partitioned into n_splits sets (contiguous chunks on the vector-unit
+// kernel, dealt 32-key tiles on the matrix-core kernel); each set's
 // unnormalised online-softmax state (m, l, acc) is computed independently and
 // the states are folded with the monoid merge ("Tang, a compiler that derives
 // GPU kernels and bounds how fast they can run", Abstract: online softmax as
 // a monoid; "Compilers and Kernels", FlashAttention section, the recurrence's
-// state and O_i = o_T / l_T).  Scoring one token is a matrix-vector product,
-// so the split kernel is bound by streaming K and V from HBM: it reads each
-// key/value row once for all query heads that share it, and issues all of a
-// sub-chunk's K and V loads before using any of them.
+// state and O_i = o_T / l_T), which is associative and commutative, so any
+// partition gives the same result up to rounding.  Scoring one token is a
+// matrix-vector product, so the split kernels are bound by streaming K and V
+// from HBM: they read each key/value row once for all query heads that share
+// it, with the next tile's loads in flight while a tile is used.
 #include "common.h"
 #include "launch.h"
 
