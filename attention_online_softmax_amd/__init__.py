@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     AttnError,
     attn_abi_version,
     attn_bwd,
+    attn_bwd_fused,
+    attn_bwd_fused_workspace_bytes,
     attn_bwd_workspace_bytes,
     attn_decode,
     attn_decode_paged,

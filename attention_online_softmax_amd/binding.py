@@ -24,7 +24,8 @@ STATUS_NAMES = {
 }
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
-           "attn_bwd_workspace_bytes", "attn_bwd", "attn_set_timing_events")
+           "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_fused_workspace_bytes",
+           "attn_bwd_fused", "attn_set_timing_events")
 
 _lib = None
 
@@ -66,6 +67,11 @@ def lib():
     L.attn_bwd.restype = i
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                            i, i, i, i, i, i, i, i, vp, i64, i64, f, vp, sz, vp]
+    L.attn_bwd_fused_workspace_bytes.restype = sz
+    L.attn_bwd_fused_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_bwd_fused.restype = i
+    L.attn_bwd_fused.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 i, i, i, i, i, i, i, f, vp, sz, vp]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -257,4 +263,33 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
                         workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_fused_workspace_bytes(B, Hq, Sq, d):
+    return int(lib().attn_bwd_fused_workspace_bytes(B, Hq, Sq, d))
+
+
+def attn_bwd_fused(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
+                   workspace=None, stream=None):
+    """Fused backward (dQ through fp32 atomic adds; no window or bias).
+    Returns (dq, dk, dv)."""
+    _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_fused_workspace_bytes(B, Hq, Sq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    st = lib().attn_bwd_fused(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
+                              int(bool(causal)), float(scale), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(),
+                              _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_bwd_fused")
     return dq, dk, dv

@@ -116,6 +116,7 @@ int attn_supports(int dtype, int entry, int d) {
     case 1: return decode_d_ok(dtype, d);
     case 2: return bwd_d_ok(dtype, d);
     case 3: return paged_d_ok(dtype, d);
+    case 4: return bwd_d_ok(dtype, d);
   }
   return 0;
 }
@@ -265,6 +266,44 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
                   causal ? 1 : 0, window > 0 ? window : 0, bias, bias_sb, bias_sh, scale,
                   (float*)workspace, (hipStream_t)stream};
   return hip_status(attn::launch_bwd(a));
+}
+
+size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0) return 0;
+  return round256((size_t)attn::bwd_fused_acc_offset(B, Hq, Sq) * sizeof(float) +
+                  (size_t)B * Hq * Sq * d * sizeof(float));
+}
+
+attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, void* dq, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  // The (D, nl) pairs are addressed with 32-bit byte offsets.
+  if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
+  if (!bwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  const size_t ws_need = attn_bwd_fused_workspace_bytes(B, Hq, Sq, d);
+  if (workspace_bytes < ws_need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  const int es = esize(dtype);
+  const int64_t nq = (int64_t)B * Hq * Sq * d * es, nkv = (int64_t)B * Hkv * Skv * d * es;
+  const Span ins[6] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
+                       span(lse, (int64_t)B * Hq * Sq * 4)};
+  const Span outs[4] = {span(dq, nq), span(dk, nkv), span(dv, nkv),
+                        span(workspace, (int64_t)ws_need)};
+  const attn_status st = check_alias(outs, 4, ins, 6);
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
+                  causal ? 1 : 0, 0, nullptr, 0, 0, scale, (float*)workspace, (hipStream_t)stream};
+  return hip_status(attn::launch_bwd_fused(a));
 }
 
 }  // extern "C"

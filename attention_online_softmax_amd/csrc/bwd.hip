@@ -11,9 +11,16 @@
 // Two kernels: dQ per query tile, which also forms D and -LSE log2(e) per
 // query row and passes them on through the workspace; then dK and dV per key
 // tile (looping over the query tiles and the query heads of a grouped
-// key/value head, so every dK/dV element is written once).  No atomics.  Both product kernels stream their tiles HBM -> LDS with
-// global_load_lds into double-buffered, swizzled tiles (see common.h) that
-// are read both by rows and, through transpose reads, by columns.
+// key/value head, so every dK/dV element is written once).  No atomics.  Both
+// product kernels stream their tiles HBM -> LDS with loads to LDS into
+// double-buffered, swizzled tiles (see common.h) that are read both by rows
+// and, through transpose reads, by columns.
+//
+// The fused variant runs the dK/dV kernel once with dQ folded in: each key
+// tile adds its share dS K to an fp32 dQ accumulator with atomic adds, so the
+// order of the additions, and with it the last bits of dQ, can change from
+// run to run.  A small kernel forms the (D, -LSE log2(e)) pairs and clears the
+// accumulator before it, another scales and rounds dQ to bf16 after it.
 #include <type_traits>
 
 #include "common.h"
@@ -50,14 +57,21 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 // the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands dO^T
 // and Q^T come from transpose reads of the same tiles.  The loop covers the
 // query tiles of all query heads of the group.
+//
+// FUSED: the K and V roles swap (K rows of the workgroup in LDS, the lane's
+// V row in registers), and after every query tile the waves stage dS (bf16,
+// [query][key]) in LDS; wave w then forms columns 32 (w % (d/32)) .. +31 of
+// dQ_tile = dS K over its share of the 128 keys (all of them for d = 128,
+// half for d = 64), with K from transpose reads of the K rows, and adds the
+// result to the fp32 accumulator dqacc [B, Hq, Sq, d] with atomic adds.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WIN, bool BIAS>
+template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
     const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale, float scale_log2,
-    int64_t rows_pad) {
+    int64_t rows_pad, float* __restrict__ dqacc) {
   constexpr int QT = 32;   // query rows per tile
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -66,9 +80,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   // per variable and so never waits for the transfer into one slot before
   // reading another.
   constexpr int SLOT = 2 * QT * D + 4 * QT;
+  // dS staging (FUSED): 32 query rows of 128 keys, padded so that both the
+  // column writes and the row reads are free of bank conflicts.
+  constexpr int SSTR = 128 + 8;
   __shared__ __attribute__((aligned(1024))) uint16_t sT0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint16_t sT1[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[128 * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[128 * D];   // K rows when FUSED
+  __shared__ __attribute__((aligned(16))) uint16_t sS[FUSED ? QT * SSTR : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -98,11 +116,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   const int n_qt = max(0, (q_end - q_start + QT - 1) / QT);
   const int n_it = G * n_qt;
 
-  // The workgroup's V rows (rows past Skv arrive as zeros).
+  // The workgroup's V rows, K rows when FUSED (rows past Skv arrive as zeros).
   {
     TileDma<D, 128, 4> vdma;
     vdma.init(wave, lane);
-    vdma.load(Vh, Skv, sV, ktile * 128, wave);
+    vdma.load(FUSED ? Kh : Vh, Skv, sV, ktile * 128, wave);
   }
   TileDma<D, QT, 4> dma;
   dma.init(wave, lane);
@@ -130,10 +148,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   };
   issue(sT0);
 
+  // The lane's K row (V row when FUSED).
   u32x4 kreg[NDC];
   const int krow = min(key, Skv - 1);
+  const uint16_t* Rh = FUSED ? Vh : Kh;
 #pragma unroll
-  for (int c = 0; c < NDC; ++c) kreg[c] = *(const u32x4*)(Kh + (int64_t)krow * D + c * 16 + 8 * g);
+  for (int c = 0; c < NDC; ++c) kreg[c] = *(const u32x4*)(Rh + (int64_t)krow * D + c * 16 + 8 * g);
 
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -160,6 +180,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     for (int i = 0; i < 16; ++i)
       bv[i] = bp[(int64_t)min(qs + 16 * (i >> 3) + 8 * g + (i & 7), Sq - 1) * Skv];
   };
+  // FUSED: dS of the lane's key for queries 16c + 8g + 0..7 into column
+  // `kl` of the staging rows.
+  const int kl = wave * 32 + swap23(n);
+  auto stage_ds = [&](int c, const u32x4& v) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sS[(16 * c + 8 * g + j) * SSTR + kl] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+  };
   auto step = [&](const uint16_t* slot, int qs, int hh) {
     const uint16_t* cQ = slot;
     const uint16_t* cG = slot + QT * D;
@@ -172,13 +200,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
       const int o = row_off<D>(r_off, c);
-      s = mfma32(lds_row(cQ, o), kreg[c], s);
-      dp = mfma32(lds_row(cG, o), lds_row(sVw, o), dp);
+      s = mfma32(lds_row(cQ, o), FUSED ? lds_row(sVw, o) : kreg[c], s);
+      dp = mfma32(lds_row(cG, o), FUSED ? kreg[c] : lds_row(sVw, o), dp);
     }
     // The softmax step and the products in two halves of 16 queries, so only
-    // half of P and dS is live at a time.
+    // half of P and dS is live at a time.  FUSED also masks keys past Skv,
+    // whose dS would otherwise enter dQ.
     const bool masked = (CAUSAL && key0_wave + 31 > qs + off) ||
-                        (win && key0_wave < qs + QT + off - window);
+                        (win && key0_wave < qs + QT + off - window) ||
+                        (FUSED && key0_wave + 31 >= Skv);
     // Element (c, j) is query qs + 16c + 8g + j: visible iff lo <= 16c + j
     // (causal) and 16c + j <= hi (window).
     const int lo = key - off - qs - 8 * g;
@@ -198,7 +228,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
           const float dd = dn[j >> 1][2 * (j & 1)];
           const float nl = dn[j >> 1][2 * (j & 1) + 1];
           float p = fast_exp2(fmaf(s[i], scale_log2, BIAS ? fmaf(bv[i], kLog2e, nl) : nl));
-          if constexpr (decltype(msk)::value) p = (16 * c + j >= lo && 16 * c + j <= hi) ? p : 0.f;
+          if constexpr (decltype(msk)::value)
+            p = ((!CAUSAL || 16 * c + j >= lo) && 16 * c + j <= hi && (!FUSED || kvalid)) ? p
+                                                                                      : 0.f;
           pv[j] = p;
           dsv[j] = p * (dp[i] - dd);
         }
@@ -212,11 +244,53 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         softmax(std::true_type{});
       else
         softmax(std::false_type{});
+      if constexpr (FUSED) stage_ds(c, dsb);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         dvt[db] = mfma32(tr_col8<D>(cG + 16 * c * D, t_off, db), pb, dvt[db]);
         dkt[db] = mfma32(tr_col8<D>(cQ + 16 * c * D, t_off, db), dsb, dkt[db]);
       }
+    }
+  };
+
+  // FUSED: dQ[qs .. qs+31, 32 qdb .. +31] += dS[:, kb0 .. kb0+KW-1] K[kb0 .., :]
+  // for query head hh; element i of lane (n, g) is query 8(i/4) + 4g + i%4,
+  // column 32 qdb + n, so each atomic instruction covers 128 contiguous bytes
+  // of two rows.  The atomics go through one descriptor per 8-row group of
+  // the tile, over the group's rows below Sq: rows past Sq fall outside its
+  // range and are dropped (the offsets are per-lane and immediate, both of
+  // which the range check covers).
+  constexpr int KW = 128 * NDB / 4;   // keys per wave in the dQ product
+  const int qdb = wave % NDB, kb0 = (wave / NDB) * KW;
+  const int dq_voff = (4 * g * D + qdb * 32 + n) * 4;
+  auto dq_tile = [&](int qs, int hh) {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KW / 16; ++c) {
+      const int kr = kb0 + 16 * c;
+      // Keys of a wave that skipped this tile have no dS staged.
+      if (CAUSAL && qs + QT - 1 + off < ktile * 128 + (kr & ~31)) continue;
+      const u32x4 a = *(const u32x4*)(sS + n * SSTR + kr + 8 * g);
+      acc = mfma32(a, tr_col8<D>(sV + kr * D, t_off, qdb), acc);
+    }
+    // Reads of step c + 1 while step c multiplies: a short lookahead keeps
+    // the registers of this phase within the budget of two waves per SIMD.
+#pragma unroll
+    for (int c = 0; c < KW / 16; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      if (c > 0) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const float* tile = dqacc + ((int64_t)(b * Hq + hk * G + hh) * Sq + qs) * D;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const rsrc_t rs = make_rsrc(tile + 8 * gq * D, (uint32_t)(max(0, min(Sq - qs - 8 * gq, 8)) * D * 4));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * gq + r], rs, dq_voff + r * D * 4,
+                                                        0, 0);
     }
   };
 
@@ -234,10 +308,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
       ++cur_hh;
     }
     // Tiles whose queries all precede this wave's first visible key, or
-    // whose windows all start after its last key: skip.
-    if (CAUSAL && qs + QT - 1 + off < key0_wave) return;
-    if (win && qs + off - window + 1 > key0_wave + 31) return;
-    step(cur, qs, hh);
+    // whose windows all start after its last key: skip (FUSED: the dQ
+    // product leaves out the keys of waves that skip).
+    const bool skip = (CAUSAL && qs + QT - 1 + off < key0_wave) ||
+                      (win && qs + off - window + 1 > key0_wave + 31);
+    if (!skip) step(cur, qs, hh);
+    if constexpr (FUSED) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's dS writes are done
+      lds_barrier();                        // ... and every wave's
+      dq_tile(qs, hh);
+    }
   };
 #pragma clang loop unroll(disable)
   for (int i = 0; i < n_it; i += 2) {
@@ -465,11 +545,11 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
   timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_ktiles * BHk), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN, BIAS, false>), dim3(n_ktiles * BHk), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
                      BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb,
-                     a.bias_sh, a.scale, sl2, rows_pad);
+                     a.bias_sh, a.scale, sl2, rows_pad, nullptr);
   timing_mark(a.stream, 3);
   return hipGetLastError();
 }
@@ -501,6 +581,116 @@ static hipError_t dispatch_bwd(const BwdArgs& a) {
 
 hipError_t launch_bwd(const BwdArgs& a) {
   return a.causal ? dispatch_bwd<true>(a) : dispatch_bwd<false>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Fused backward: bwd_prep_kernel, the dK/dV kernel with dQ folded in, then
+// bwd_dq_convert_kernel.
+// ---------------------------------------------------------------------------
+
+// Per padded query row r of [B * Hq, Sqp]: the pair (D_r, nl_r) exactly as
+// the dQ kernel forms it ((0, -inf) for padding rows; the same products and
+// order of additions, so the dK/dV kernel sees the same values) and a zeroed
+// dQ accumulator row.  Two threads per row: thread h takes the columns
+// 16c + 8h .. 16c + 8h + 7.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
+                                                       const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ ws,
+                                                       float* __restrict__ dqacc,
+                                                       int64_t rows_pad, int Sq, int Sqp) {
+  constexpr int NDC = D / 16;
+  const int64_t r = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 1);
+  const int h = threadIdx.x & 1;
+  if (r >= rows_pad) return;   // both threads of a row leave together
+  const int64_t bh = r / Sqp;
+  const int i = (int)(r - bh * Sqp);
+  if (i >= Sq) {
+    if (h == 0) *(f32x2*)(ws + 2 * r) = f32x2{0.f, kNegInf};
+    return;
+  }
+  const int64_t row = bh * Sq + i;
+  const uint16_t* o = O + row * D + 8 * h;
+  const uint16_t* go = dO + row * D + 8 * h;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    const u32x4 x = *(const u32x4*)(o + 16 * c);
+    const u32x4 y = *(const u32x4*)(go + 16 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(x[e] << 16), __uint_as_float(y[e] << 16), acc);
+      acc = fmaf(__uint_as_float(x[e] & 0xffff0000u), __uint_as_float(y[e] & 0xffff0000u), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  if (h == 0) {
+    const float lse = LSE[row];
+    *(f32x2*)(ws + 2 * r) = f32x2{acc, lse != kNegInf ? -lse * kLog2e : kNegInf};
+  }
+  float* z = dqacc + row * D + h * (D / 2);
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) *(f32x4*)(z + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = scale * dqacc rounded to bf16, eight elements per thread.
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ dqacc,
+                                                             uint16_t* __restrict__ dQ, int64_t n8,
+                                                             float scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 x = *(const f32x4*)(dqacc + 8 * i);
+  const f32x4 y = *(const f32x4*)(dqacc + 8 * i + 4);
+  *(u32x4*)(dQ + 8 * i) =
+      u32x4{pack_bf16x2(x[0] * scale, x[1] * scale), pack_bf16x2(x[2] * scale, x[3] * scale),
+            pack_bf16x2(y[0] * scale, y[1] * scale), pack_bf16x2(y[2] * scale, y[3] * scale)};
+}
+
+// Offset of the dQ accumulator in the fused workspace, in floats: after the
+// (D, nl) pairs, rounded up to 256 bytes.
+int64_t bwd_fused_acc_offset(int B, int Hq, int Sq) {
+  const int64_t sqp = ((int64_t)Sq + 31) / 32 * 32;
+  return (2 * (int64_t)B * Hq * sqp + 63) / 64 * 64;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_fused_t(const BwdArgs& a) {
+  const int Sqp = (a.Sq + 31) / 32 * 32;
+  const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
+  const float sl2 = a.scale * kLog2e;
+  float* dqacc = a.ws + bwd_fused_acc_offset(a.B, a.Hq, a.Sq);
+  timing_mark(a.stream, 0);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows_pad + 127) / 128)), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, dqacc,
+                     rows_pad, a.Sq, Sqp);
+  timing_mark(a.stream, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (a.Skv + 127) / 128;
+  const int BHk = a.B * a.Hkv;
+  timing_mark(a.stream, 2);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(n_ktiles * BHk),
+                     dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, 0,
+                     nullptr, 0, 0, a.scale, sl2, rows_pad, dqacc);
+  timing_mark(a.stream, 3);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n8 = (int64_t)a.B * a.Hq * a.Sq * D / 8;
+  timing_mark(a.stream, 4);
+  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     a.stream, (const float*)dqacc, (uint16_t*)a.dq, n8, a.scale);
+  timing_mark(a.stream, 5);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_bwd_fused_t<64, true>(a) : launch_bwd_fused_t<64, false>(a);
+  if (a.d == 128)
+    return a.causal ? launch_bwd_fused_t<128, true>(a) : launch_bwd_fused_t<128, false>(a);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attn

@@ -73,5 +73,9 @@ void timing_mark(hipStream_t stream, int slot);
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+// Fused variant (no window or bias): ws holds the (D, nl) pairs, then from
+// bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].
+hipError_t launch_bwd_fused(const BwdArgs& a);
+int64_t bwd_fused_acc_offset(int B, int Hq, int Sq);
 
 }  // namespace attn

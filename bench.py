@@ -446,6 +446,66 @@ def bench_masked(args, hev, stream, reps, window=0, with_bias=False):
             "frac_of_bf16_peak": 3.5 * flop_fwd / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_fused_bwd(args, hev, stream, reps):
+    """Backward of the training shape (B4 H16 S2048 d128, causal) two ways:
+    the two-kernel attn_bwd (dQ kernel, then dK/dV) and attn_bwd_fused (one
+    pass over the key tiles, dQ added with fp32 atomics).  Reports the call
+    times, the fused call's kernels and the bytes its atomics add."""
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    w = WORKLOADS["train_fwd_bwd"]
+    sets = [{k: v.cuda() for k, v in make_workload(w, w.seed_base + 100 * i).items()}
+            for i in range(3)]
+    outs = []
+    for s in sets:
+        o, lse = aos.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w.scale)
+        outs.append(dict(o=o, lse=lse, dq=torch.empty_like(s["q"]), dk=torch.empty_like(s["k"]),
+                         dv=torch.empty_like(s["v"]),
+                         ws=torch.empty(aos.attn_bwd_workspace_bytes(w.B, w.Hq, w.Sq, w.d),
+                                        device="cuda", dtype=torch.uint8),
+                         wsf=torch.empty(aos.attn_bwd_fused_workspace_bytes(w.B, w.Hq, w.Sq, w.d),
+                                         device="cuda", dtype=torch.uint8)))
+
+    def two(i):
+        s, o = sets[i % 3], outs[i % 3]
+        aos.attn_bwd(s["q"], s["k"], s["v"], o["o"], s["do"], o["lse"], causal=True, scale=w.scale,
+                     dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["ws"])
+
+    def fused(i):
+        s, o = sets[i % 3], outs[i % 3]
+        aos.attn_bwd_fused(s["q"], s["k"], s["v"], o["o"], s["do"], o["lse"], causal=True,
+                           scale=w.scale, dq=o["dq"], dk=o["dk"], dv=o["dv"], workspace=o["wsf"])
+
+    for i in range(3):
+        two(i)
+        fused(i)
+    torch.cuda.synchronize()
+    _, times, spans = run_calls([("two", two), ("fused", fused)], {"two": 2, "fused": 3}, hev,
+                                reps, stream)
+    tq = quantiles([t for t in spans["two"] if t is not None])
+    fq = quantiles([t for t in spans["fused"] if t is not None])
+    names = ("prep_kernel", "dkdv_dq_fused_kernel", "dq_convert_kernel")
+    kern = {nm: quantiles([t[i] for t in times["fused"] if t[i] is not None])["median"] * 1e3
+            for i, nm in enumerate(names)}
+    # fp32 bytes added by the atomics: per (128-key tile, 32-query tile) pair
+    # that the causal loop visits, min(32, Sq - q0) rows of d floats.
+    off = w.Skv - w.Sq
+    atom = 0
+    for kt in range((w.Skv + 127) // 128):
+        q0 = max(0, kt * 128 - off) // 32 * 32
+        for qs in range(q0, w.Sq, 32):
+            atom += min(32, w.Sq - qs) * w.d * 4
+    atom *= w.B * w.Hq
+    flop_bwd = 2.5 * flops_fwd(w)
+    return {"workload": "train shape bf16 causal B4 H16 S2048 d128, backward only",
+            "two_kernel_us": tq["median"] * 1e3, "fused_us": fq["median"] * 1e3,
+            "two_kernel_TFLOP/s": flop_bwd / (tq["median"] * 1e-3) / 1e12,
+            "fused_TFLOP/s": flop_bwd / (fq["median"] * 1e-3) / 1e12,
+            "fused_kernels_us": kern, "dq_atomic_bytes": atom,
+            "dq_atomic_GB/s_over_fused_kernel": atom / (kern["dkdv_dq_fused_kernel"] * 1e-6) / 1e9}
+
+
 def measured_ceilings(stream):
     """What the box reaches, as the measured ceilings beside the spec peaks:
     HBM read bandwidth of a grid-stride streaming read of 1 GiB (three
@@ -576,6 +636,9 @@ def main():
                                               with_bias=True)
         print(f"[bench] bias fwd+bwd: {extras['bias_fwd_bwd']['ms_per_step']:.3f} ms/step",
               file=sys.stderr, flush=True)
+        extras["fused_bwd"] = bench_fused_bwd(args, hev, stream, max(args.steps, 20))
+        print(f"[bench] backward two-kernel {extras['fused_bwd']['two_kernel_us']:.1f} us, "
+              f"fused {extras['fused_bwd']['fused_us']:.1f} us", file=sys.stderr, flush=True)
         extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
         print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",
               file=sys.stderr, flush=True)

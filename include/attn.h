@@ -80,7 +80,8 @@ int attn_abi_version(void);
 const char* attn_status_str(int status);
 
 /* Head dims compiled for (dtype, entry point): returns 1 if supported.
- * entry: 0 = attn_fwd, 1 = attn_decode, 2 = attn_bwd, 3 = attn_decode_paged. */
+ * entry: 0 = attn_fwd, 1 = attn_decode, 2 = attn_bwd, 3 = attn_decode_paged,
+ * 4 = attn_bwd_fused. */
 int attn_supports(int dtype, int entry, int d);
 
 /*
@@ -213,6 +214,36 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
                      int64_t bias_sh, float scale,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace for attn_bwd_fused: the attn_bwd workspace rounded up to 256
+ * bytes, then B * Hq * Sq * d float32 values (the dQ accumulator), the total
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d);
+
+/*
+ * Fused backward: the gradients of attn_bwd (same formulas and arguments,
+ * without window and bias) from one pass over the key tiles: the fused
+ * kernel form of the backward that "Tang, a compiler that derives GPU
+ * kernels and bounds how fast they can run" reports for CUDA in its Abstract
+ * (a flash-style backward with no intermediates written, computing in bf16
+ * and therefore outside an f32 tolerance).  Each workgroup owns 128 keys, forms dK and
+ * dV for them while it loops over the query tiles, and adds its share
+ * scale dS K of every query tile's dQ to a float32 accumulator in the
+ * workspace with atomic adds; a last kernel rounds the accumulator to dq.
+ * Three kernels per call: the (D, -lse log2 e) pairs with the accumulator
+ * cleared, the fused dK/dV/dQ kernel, the dQ rounding.
+ * Because the additions into the accumulator happen in no fixed order, dq
+ * may differ in its last bits from call to call (dk and dv do not).
+ *   workspace >= attn_bwd_fused_workspace_bytes(B, Hq, Sq, d) bytes,
+ *   16-byte aligned; contents on entry are ignored, on exit unspecified.
+ * Errors as attn_bwd.  Supported: bf16 with d in {64, 128}.
+ */
+attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* v,
+                           const void* o, const void* d_o, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                           int causal, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles
  * created by the caller.  While set (per calling host thread), every entry
@@ -221,7 +252,7 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
  * the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
  * (the forward kernel), attn_decode and attn_decode_paged 2 (split,
  * combine), attn_bwd 2
- * (dQ together with D = rowsum(dO*O), then dK/dV).  Pass NULL or n = 0 to stop.  The library
+ * (dQ together with D = rowsum(dO*O), then dK/dV), attn_bwd_fused 3.  Pass NULL or n = 0 to stop.  The library
  * neither creates nor destroys the events.  Returns ATTN_ERR_VALUE if n < 0.
  */
 attn_status attn_set_timing_events(void* const* events, int n);

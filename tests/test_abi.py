@@ -52,6 +52,8 @@ def test_supports():
     assert not aos.attn_supports(BF16, 2, 256)
     assert aos.attn_supports(BF16, 3, 64) and aos.attn_supports(BF16, 3, 128)
     assert not aos.attn_supports(BF16, 3, 256) and not aos.attn_supports(F32, 3, 128)
+    assert aos.attn_supports(BF16, 4, 64) and aos.attn_supports(BF16, 4, 128)
+    assert not aos.attn_supports(BF16, 4, 256) and not aos.attn_supports(F32, 4, 64)
     assert not aos.attn_supports(BF16, 0, 96)
     assert not aos.attn_supports(7, 0, 64)
 
@@ -63,6 +65,12 @@ def test_workspace_sizes():
     assert aos.attn_bwd_workspace_bytes(4, 16, 2048, 128) == 2 * 4 * 16 * 2048 * 4
     assert aos.attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
     assert aos.attn_bwd_workspace_bytes(1, -1, 1, 64) == 0
+    # fused: the pairs rounded up to 256 bytes, then the fp32 dQ accumulator
+    assert aos.attn_bwd_fused_workspace_bytes(4, 16, 2048, 128) == \
+        2 * 4 * 16 * 2048 * 4 + 4 * 16 * 2048 * 128 * 4
+    assert aos.attn_bwd_fused_workspace_bytes(1, 1, 1, 64) == 256 + 256
+    assert aos.attn_bwd_fused_workspace_bytes(1, 1, 3, 64) == 256 + 768
+    assert aos.attn_bwd_fused_workspace_bytes(0, 1, 1, 64) == 0
 
 
 class Fake:
@@ -211,6 +219,39 @@ def test_bwd_validation():
     assert call(bias=p["ws"]) == ALIAS               # the bias overlaps the workspace
     assert call(bias=f() + 8) == ALIGN
     assert call(bias=f(), sb=-8) == VALUE
+
+
+def test_bwd_fused_validation():
+    f = Fake()
+    names = ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws")
+    p = {n: f() for n in names}
+    need = aos.attn_bwd_fused_workspace_bytes(1, 4, 64, 128)
+    L = aos.lib()
+
+    def call(**kw):
+        a = dict(p)
+        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, scale=0.1,
+                      wsb=need))
+        a.update(kw)
+        return L.attn_bwd_fused(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                a["dq"], a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                                a["Skv"], a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], None)
+
+    for n in names[:-1]:
+        assert call(**{n: None}) == NULL, n
+    assert call(Sq=65) == SHAPE
+    assert call(Hq=5) == SHAPE
+    assert call(B=0) == SHAPE
+    assert call(d=256) == UNSUP
+    assert call(dt=F32) == UNSUP
+    assert call(scale=float("nan")) == VALUE
+    assert call(ws=None) == WS
+    assert call(wsb=need - 256) == WS        # room for the pairs but not the accumulator
+    assert call(dk=p["dv"]) == ALIAS
+    assert call(dq=p["do"]) == ALIAS
+    assert call(ws=p["lse"]) == ALIAS
+    assert call(dv=p["dv"] + 2) == ALIGN
+    assert call(ws=p["ws"] + 8) == ALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
