@@ -583,113 +583,27 @@ hipError_t launch_bwd(const BwdArgs& a) {
   return a.causal ? dispatch_bwd<true>(a) : dispatch_bwd<false>(a);
 }
 
-// ---------------------------------------------------------------------------
-// Fused backward: bwd_prep_kernel, the dK/dV kernel with dQ folded in, then
-// bwd_dq_convert_kernel.
-// ---------------------------------------------------------------------------
-
-// Per padded query row r of [B * Hq, Sqp]: the pair (D_r, nl_r) exactly as
-// the dQ kernel forms it ((0, -inf) for padding rows; the same products and
-// order of additions, so the dK/dV kernel sees the same values) and a zeroed
-// dQ accumulator row.  Two threads per row: thread h takes the columns
-// 16c + 8h .. 16c + 8h + 7.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
-                                                       const uint16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ ws,
-                                                       float* __restrict__ dqacc,
-                                                       int64_t rows_pad, int Sq, int Sqp) {
-  constexpr int NDC = D / 16;
-  const int64_t r = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 1);
-  const int h = threadIdx.x & 1;
-  if (r >= rows_pad) return;   // both threads of a row leave together
-  const int64_t bh = r / Sqp;
-  const int i = (int)(r - bh * Sqp);
-  if (i >= Sq) {
-    if (h == 0) *(f32x2*)(ws + 2 * r) = f32x2{0.f, kNegInf};
-    return;
-  }
-  const int64_t row = bh * Sq + i;
-  const uint16_t* o = O + row * D + 8 * h;
-  const uint16_t* go = dO + row * D + 8 * h;
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < NDC; ++c) {
-    const u32x4 x = *(const u32x4*)(o + 16 * c);
-    const u32x4 y = *(const u32x4*)(go + 16 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(x[e] << 16), __uint_as_float(y[e] << 16), acc);
-      acc = fmaf(__uint_as_float(x[e] & 0xffff0000u), __uint_as_float(y[e] & 0xffff0000u), acc);
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  if (h == 0) {
-    const float lse = LSE[row];
-    *(f32x2*)(ws + 2 * r) = f32x2{acc, lse != kNegInf ? -lse * kLog2e : kNegInf};
-  }
-  float* z = dqacc + row * D + h * (D / 2);
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) *(f32x4*)(z + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// dQ = scale * dqacc rounded to bf16, eight elements per thread.
-__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ dqacc,
-                                                             uint16_t* __restrict__ dQ, int64_t n8,
-                                                             float scale) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x = *(const f32x4*)(dqacc + 8 * i);
-  const f32x4 y = *(const f32x4*)(dqacc + 8 * i + 4);
-  *(u32x4*)(dQ + 8 * i) =
-      u32x4{pack_bf16x2(x[0] * scale, x[1] * scale), pack_bf16x2(x[2] * scale, x[3] * scale),
-            pack_bf16x2(y[0] * scale, y[1] * scale), pack_bf16x2(y[2] * scale, y[3] * scale)};
-}
-
-// Offset of the dQ accumulator in the fused workspace, in floats: after the
-// (D, nl) pairs, rounded up to 256 bytes.
-int64_t bwd_fused_acc_offset(int B, int Hq, int Sq) {
-  const int64_t sqp = ((int64_t)Sq + 31) / 32 * 32;
-  return (2 * (int64_t)B * Hq * sqp + 63) / 64 * 64;
-}
-
+// The dK/dV kernel with dQ folded in, for the fused backward (bwd_fused.hip
+// forms the pairs and clears dqacc before it, and rounds dQ after it).
 template <int D, bool CAUSAL>
-static hipError_t launch_bwd_fused_t(const BwdArgs& a) {
+static hipError_t launch_dkdv_fused_t(const BwdArgs& a, float* dqacc) {
   const int Sqp = (a.Sq + 31) / 32 * 32;
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
-  const float sl2 = a.scale * kLog2e;
-  float* dqacc = a.ws + bwd_fused_acc_offset(a.B, a.Hq, a.Sq);
-  timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows_pad + 127) / 128)), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, dqacc,
-                     rows_pad, a.Sq, Sqp);
-  timing_mark(a.stream, 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
-  timing_mark(a.stream, 2);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(n_ktiles * BHk),
                      dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, 0,
-                     nullptr, 0, 0, a.scale, sl2, rows_pad, dqacc);
-  timing_mark(a.stream, 3);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n8 = (int64_t)a.B * a.Hq * a.Sq * D / 8;
-  timing_mark(a.stream, 4);
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                     a.stream, (const float*)dqacc, (uint16_t*)a.dq, n8, a.scale);
-  timing_mark(a.stream, 5);
+                     nullptr, 0, 0, a.scale, a.scale * kLog2e, rows_pad, dqacc);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_fused(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_bwd_fused_t<64, true>(a) : launch_bwd_fused_t<64, false>(a);
-  if (a.d == 128)
-    return a.causal ? launch_bwd_fused_t<128, true>(a) : launch_bwd_fused_t<128, false>(a);
+hipError_t launch_dkdv_fused(const BwdArgs& a, float* dqacc) {
+  if (a.d == 64) return a.causal ? launch_dkdv_fused_t<64, true>(a, dqacc)
+                                 : launch_dkdv_fused_t<64, false>(a, dqacc);
+  if (a.d == 128) return a.causal ? launch_dkdv_fused_t<128, true>(a, dqacc)
+                                  : launch_dkdv_fused_t<128, false>(a, dqacc);
   return hipErrorInvalidValue;
 }
 

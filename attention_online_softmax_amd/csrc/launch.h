@@ -77,5 +77,7 @@ hipError_t launch_bwd(const BwdArgs& a);
 // bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].
 hipError_t launch_bwd_fused(const BwdArgs& a);
 int64_t bwd_fused_acc_offset(int B, int Hq, int Sq);
+// The fused dK/dV/dQ kernel alone (a.ws holds the pairs; dqacc is cleared).
+hipError_t launch_dkdv_fused(const BwdArgs& a, float* dqacc);
 
 }  // namespace attn
