@@ -119,6 +119,25 @@ __device__ __forceinline__ int tile_swz(int r) {
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 
+// Compensated (Kahan) running sum of the softmax normaliser; its value is
+// s - c.  Tile sums added to a running sum that dwarfs them lose their low
+// bits, and when they repeat (many keys with equal scores after a dominant
+// one) the loss keeps one sign and grows with the key count; c carries it.
+struct KahanSum {
+  float s, c;
+  __device__ __forceinline__ void scale(float a) {
+    s *= a;
+    c *= a;
+  }
+  __device__ __forceinline__ void add(float x) {
+    const float y = x - c;
+    const float t = s + y;
+    c = (t - s) - y;
+    s = t;
+  }
+  __device__ __forceinline__ float value() const { return s - c; }
+};
+
 // Workgroup barrier for LDS tiles filled by loads to LDS, without the
 // release/acquire fences of __syncthreads (which wait for every load in
 // flight, including prefetches of later tiles).  Callers wait for their own

@@ -184,7 +184,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   int st = 0, buf = 0;
   issue(cur, 0, 0);
 
-  float q[GC][E], m[GC], lsum[GC], acc[GC][E];
+  float q[GC][E], m[GC], acc[GC][E];
+  KahanSum lsum[GC];
   bool fresh = true;  // first stage of the current item
 
   while (true) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) q[hh][e] = f[e] * scale_log2;
         m[hh] = kNegInf;
-        lsum[hh] = 0.f;
+        lsum[hh] = KahanSum{0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
       }
@@ -266,9 +267,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
       const float mnew = fmaxf(m[hh], mx);           // finite: the stage is non-empty
       const float alpha = fast_exp2(m[hh] - mnew);   // 0 on the item's first stage
       m[hh] = mnew;
-      lsum[hh] *= alpha;
+      lsum[hh].scale(alpha);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[hh][e] *= alpha;
+    }
+    // The stage's terms are summed from zero and then added to the running
+    // (lsum, acc): added one by one, terms far below a large running value
+    // (keys after a dominant one, over millions of keys) would round away.
+    float lst[GC], ast[GC][E];
+#pragma unroll
+    for (int hh = 0; hh < GC; ++hh) {
+      lst[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ast[hh][e] = 0.f;
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -278,10 +289,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 #pragma unroll
       for (int hh = 0; hh < GC; ++hh) {
         const float pw = fast_exp2(s[hh][p] - m[hh]);
-        lsum[hh] += pw;
+        lst[hh] += pw;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pw, f[e], acc[hh][e]);
+        for (int e = 0; e < E; ++e) ast[hh][e] = fmaf(pw, f[e], ast[hh][e]);
       }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GC; ++hh) {
+      lsum[hh].add(lst[hh]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[hh][e] += ast[hh][e];
     }
 
     if (st + 1 >= cur.n_st) {
@@ -289,7 +306,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
       // waves through LDS) and write its state.
 #pragma unroll
       for (int hh = 0; hh < GC; ++hh) {
-        float l = lsum[hh];  // identical across the lanes of a row group
+        float l = lsum[hh].value();  // identical across the lanes of a row group
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           float x = acc[hh][e];
@@ -513,7 +530,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
   issue(cur, 0, PAGED ? load_pid(cur, 0) : 0, sKa[wave], sVa[wave]);
   int t = 0;
   bool new_q = false;
-  float m_ref = kNegInf, lpart = 0.f;
+  float m_ref = kNegInf;
+  KahanSum lpart{0.f, 0.f};
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -574,7 +592,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
     if (__any(mnew > m_ref + kDecodeLazy)) {
       const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
-      lpart *= alpha;
+      lpart.scale(alpha);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -583,15 +601,17 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
     }
     const float msub = (m_ref == kNegInf) ? 0.f : m_ref;
     u32x4 pb[2];
+    float tl = 0.f;   // the tile's sum, added to lpart as one term
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p0 = fast_exp2(fmaf(s[8 * c + 2 * j], c2, -msub));
         const float p1 = fast_exp2(fmaf(s[8 * c + 2 * j + 1], c2, -msub));
-        lpart += p0 + p1;
+        tl += p0 + p1;
         pb[c][j] = pack_bf16x2(p0, p1);
       }
+    lpart.add(tl);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -600,10 +620,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
                           oacc[db]);
 
     if (unit_end) {
-      write_state(cur, m_ref, lpart, oacc);
+      write_state(cur, m_ref, lpart.value(), oacc);
       if (!more) return false;
       m_ref = kNegInf;
-      lpart = 0.f;
+      lpart = KahanSum{0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -39,14 +39,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const float* Kh = K + ((int64_t)(b * Hkv + hk) * Skv) * D;
   const float* Vh = V + ((int64_t)(b * Hkv + hk) * Skv) * D;
 
-  float q[32], o[32];
+  float q[32];
+  KahanSum o[32];   // compensated, like the normaliser
   const bool valid = row < Sq;
 #pragma unroll
   for (int c = 0; c < 32; c += 4) {
     f32x4 x = valid ? *(const f32x4*)(Qh + (int64_t)row * D + col0 + c) : f32x4{0, 0, 0, 0};
     q[c] = x[0]; q[c + 1] = x[1]; q[c + 2] = x[2]; q[c + 3] = x[3];
-    o[c] = o[c + 1] = o[c + 2] = o[c + 3] = 0.f;
   }
+#pragma unroll
+  for (int c = 0; c < 32; ++c) o[c] = KahanSum{0.f, 0.f};
   // Keys [row_lo, row_limit); a sliding window of `window` keys (causal
   // only, 0 = none) raises the lower end.
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
@@ -59,7 +61,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const float* brow =
       bias ? bias + b * bsb + h * bsh + (int64_t)min(row, Sq - 1) * Skv : nullptr;
 
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf;
+  KahanSum l{0.f, 0.f};
   for (int k0 = kv_begin; k0 < kv_end; k0 += BC) {
     __syncthreads();
     for (int e = tid * 4; e < BC * D; e += 256 * 4) {
@@ -98,32 +101,44 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     }
     const float msub = (mx == kNegInf) ? 0.f : mx;
     const float alpha = fast_exp2(m - msub);
-    l *= alpha;
+    // The tile's terms are summed from zero, then added to the rescaled
+    // running (l, o): one by one, terms far below a large running value
+    // would round away over long sequences.
+    float lt = 0.f, ot[32];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] *= alpha;
+    for (int c = 0; c < 32; ++c) ot[c] = 0.f;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
       const float p = fast_exp2(s[j] - msub);
-      l += p;
+      lt += p;
 #pragma unroll
       for (int c = 0; c < 32; c += 4) {
         f32x4 vx = *(const f32x4*)(sV + j * D + col0 + c);
-        o[c] = fmaf(p, vx[0], o[c]);
-        o[c + 1] = fmaf(p, vx[1], o[c + 1]);
-        o[c + 2] = fmaf(p, vx[2], o[c + 2]);
-        o[c + 3] = fmaf(p, vx[3], o[c + 3]);
+        ot[c] = fmaf(p, vx[0], ot[c]);
+        ot[c + 1] = fmaf(p, vx[1], ot[c + 1]);
+        ot[c + 2] = fmaf(p, vx[2], ot[c + 2]);
+        ot[c + 3] = fmaf(p, vx[3], ot[c + 3]);
       }
+    }
+    l.scale(alpha);
+    l.add(lt);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      o[c].scale(alpha);
+      o[c].add(ot[c]);
     }
     m = mx;
   }
   if (!valid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
+  const float lv = l.value();
+  const float inv = lv > 0.f ? 1.f / lv : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   float* Oh = O + ((int64_t)bh * Sq + row) * D + col0;
 #pragma unroll
   for (int c = 0; c < 32; c += 4) {
-    *(f32x4*)(Oh + c) = f32x4{o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
+    *(f32x4*)(Oh + c) = f32x4{o[c].value() * inv, o[c + 1].value() * inv,
+                              o[c + 2].value() * inv, o[c + 3].value() * inv};
   }
-  if (LSE && (tid % TPR) == 0) LSE[(int64_t)bh * Sq + row] = (m + fast_log2(l)) * kLn2;
+  if (LSE && (tid % TPR) == 0) LSE[(int64_t)bh * Sq + row] = (m + fast_log2(lv)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -240,7 +255,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   row_read_offsets<D>(n, g, k_off);
   tr_read_offsets<D>(lane, v_off);
 
-  float m_ref = kNegInf, lpart = 0.f;
+  float m_ref = kNegInf;
+  KahanSum lpart{0.f, 0.f};
 
   // S^T(tile) = K(tile) Q^T for this wave's 32 queries.
   auto qk = [&](const uint16_t* cK, f32x16* s) {
@@ -314,7 +330,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       m_ref = mnew;
       lsum = exps((m_ref == kNegInf) ? 0.f : m_ref);
     }
-    lpart = fmaf(lpart, alpha, lsum);
+    lpart.scale(alpha);
+    lpart.add(lsum);
     return alpha;
   };
 
@@ -399,7 +416,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     }
   }
 
-  const float l = halfwave_sum(lpart);
+  const float l = halfwave_sum(lpart.value());
   if (!valid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   uint16_t* Orow = O + ((int64_t)bh * Sq + row) * D;
