@@ -19,7 +19,7 @@ import torch
 
 import attention_online_softmax_amd as aos
 from attention_online_softmax_amd.inputs import randn, to_f64
-from tests.gpu_util import TOL_LSE, TOL_O, assert_close, note
+from tests.gpu_util import TOL_GRAD, TOL_LSE, TOL_O, assert_close, note
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +95,61 @@ def test_fwd_one_row_max_size(dt, d, Skv):
     """attn_fwd with a single query row (causal, bottom-right aligned: it sees
     every key) over the largest key count per head."""
     run_case(dt, d, Skv, 8 if dt == "bf16" else 4, 0, 4500 + d, entry="fwd")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_kernel", "fused"])
+def test_bwd_one_row_max_size(fused):
+    """Backward of one query row over 2^24 - 32 keys (bf16, d = 128, causal,
+    bottom-right aligned).  With the spike structure the gradients have
+    closed forms: P_j = e^(s_j - M) / den, dV_j = P_j dO, dS_j = P_j (dO.V_j -
+    dO.O), dK_j = scale dS_j q, dQ = scale sum_spikes dS_j K_j (the other key
+    rows are zero).  dV and dK are checked on the spike rows, the first and
+    last rows and 64 seeded random rows; dQ in full."""
+    d, Skv, seed = 128, (1 << 24) - 32, 4700
+    tdt = torch.bfloat16
+    note(f"max-size bwd fused={fused}: inputs")
+    q = randn((1, 1, 1, d), seed, 1.0, tdt).cuda()
+    do = randn((1, 1, 1, d), seed + 3, 1.0, tdt).cuda()
+    k = torch.zeros((1, 1, Skv, d), device="cuda", dtype=tdt)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    v = torch.randn((1, 1, Skv, d), device="cuda", dtype=torch.float32, generator=g).to(tdt)
+    spikes = {0: 1.5, 12345: 1.7, (1 << 23) + 7: 1.9, Skv - 33: 2.0, Skv - 1: 2.1}
+    for j, c in spikes.items():
+        k[0, 0, j] = (q[0, 0, 0].float() * c).to(tdt)
+    scale = 1 / math.sqrt(d)
+    note(f"max-size bwd fused={fused}: forward + backward")
+    o, lse = aos.attn_fwd(q, k, v, causal=True, scale=scale)
+    bwd = aos.attn_bwd_fused if fused else aos.attn_bwd
+    dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    note(f"max-size bwd fused={fused}: float64 reference")
+    qf, dof = to_f64(q)[0, 0, 0], to_f64(do)[0, 0, 0]
+    ks = {j: to_f64(k[0, 0, j]) for j in spikes}
+    vs = {j: to_f64(v[0, 0, j]) for j in spikes}
+    v_all = v_sum_f64(v)
+    n_rest = Skv - len(spikes)
+    s = {j: scale * float(qf @ ks[j]) for j in spikes}
+    M = max(0.0, max(s.values()))
+    den = sum(math.exp(s[j] - M) for j in spikes) + n_rest * math.exp(-M)
+    p = {j: math.exp(s[j] - M) / den for j in spikes}
+    p_rest = math.exp(-M) / den
+    O = sum(p[j] * vs[j] for j in spikes) + p_rest * (v_all - sum(vs.values()))
+    Dd = float(dof @ O)
+    rng = np.random.default_rng(seed)
+    rows = sorted(set(spikes) | {1, Skv // 2} | set(int(x) for x in rng.integers(0, Skv, 64)))
+    got_dv = to_f64(dv[0, 0, rows])
+    got_dk = to_f64(dk[0, 0, rows])
+    ref_dv = np.zeros((len(rows), d))
+    ref_dk = np.zeros((len(rows), d))
+    for i, j in enumerate(rows):
+        pj = p.get(j, p_rest)
+        vj = to_f64(v[0, 0, j])
+        ref_dv[i] = pj * dof
+        ref_dk[i] = scale * pj * (float(dof @ vj) - Dd) * qf
+    ref_dq = scale * sum(p[j] * (float(dof @ vs[j]) - Dd) * ks[j] for j in spikes)
+    assert_close(got_dv, ref_dv, TOL_GRAD, f"max-size bwd fused={fused} dV rows")
+    assert_close(got_dk, ref_dk, TOL_GRAD, f"max-size bwd fused={fused} dK rows")
+    assert_close(to_f64(dq)[0, 0, 0], ref_dq, TOL_GRAD, f"max-size bwd fused={fused} dQ")
+    del q, do, k, v, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
