@@ -79,6 +79,38 @@ __device__ __forceinline__ float halfwave_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// DPP lane permutations within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;      // row_ror:8 (lane i of a row reads lane (i + 8) % 16)
+
+// Sum (or max) over each aligned group of N consecutive lanes; every lane of
+// the group receives the result.  Steps: lane ^ 1, lane ^ 2 (quad perms),
+// mirror within 8 and within 16 (each pairs lanes whose partial results
+// cover disjoint halves), then lane ^ 16 (permlane16 swap: with both
+// operands x, the two results are x and x of lane ^ 16) and lane ^ 32.
+template <int N, bool MAX>
+__device__ __forceinline__ float group_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (N >= 2) x = op(x, dpp_mov<kQuadXor1>(x));
+  if constexpr (N >= 4) x = op(x, dpp_mov<kQuadXor2>(x));
+  if constexpr (N >= 8) x = op(x, dpp_mov<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = op(x, dpp_mov<kRowMirror>(x));
+  if constexpr (N >= 32) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (N >= 64) x = MAX ? halfwave_max(x) : halfwave_sum(x);
+  return x;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane L supplies the address of 4 consecutive bf16 that form row L/4,
 // columns 4*(L%4) .. 4*(L%4)+3 of a 4 x 16 block; lane j receives column j

@@ -40,38 +40,6 @@ struct Elem<uint16_t> {
   __device__ static void store2(uint16_t* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
 };
 
-// DPP lane permutations within rows of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-constexpr int kRowRor8 = 0x128;      // row_ror:8 (lane i of a row reads lane (i + 8) % 16)
-
-// Sum (or max) over each aligned group of N consecutive lanes; every lane of
-// the group receives the result.  Steps: lane ^ 1, lane ^ 2 (quad perms),
-// mirror within 8 and within 16 (each pairs lanes whose partial results
-// cover disjoint halves), then lane ^ 16 (permlane16 swap: with both
-// operands x, the two results are x and x of lane ^ 16) and lane ^ 32.
-template <int N, bool MAX>
-__device__ __forceinline__ float group_reduce(float x) {
-  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  if constexpr (N >= 2) x = op(x, dpp_mov<kQuadXor1>(x));
-  if constexpr (N >= 4) x = op(x, dpp_mov<kQuadXor2>(x));
-  if constexpr (N >= 8) x = op(x, dpp_mov<kRowHalfMirror>(x));
-  if constexpr (N >= 16) x = op(x, dpp_mov<kRowMirror>(x));
-  if constexpr (N >= 32) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
-  if constexpr (N >= 64) x = MAX ? halfwave_max(x) : halfwave_sum(x);
-  return x;
-}
-
 constexpr int kDecodeThreads = 256;
 
 // Persistent split kernel.  A work item is one key chunk (split) of one
@@ -752,16 +720,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     for (int c = 0; c < CPL; c += 2) Elem<T>::store2(o + c, a[c] * inv, a[c + 1] * inv);
   }
   if (LSE && lane == 0) LSE[bh] = (M + fast_log2(l)) * kLn2;
-}
-
-// Compute units of the current device (one persistent split workgroup each).
-static int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return cus;
 }
 
 template <typename T, int D, int GC>

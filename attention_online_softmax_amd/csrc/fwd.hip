@@ -10,17 +10,21 @@ namespace attn {
 
 // ---------------------------------------------------------------------------
 // float32 path: plain VALU arithmetic in fp32 end to end.
-// TPR = D/32 consecutive lanes share one query row, each owning 32 of its
-// columns of q and o; scores are reduced across those lanes with shuffles.
+// TPR consecutive lanes share one query row, each owning D/TPR of its
+// columns of q and o; scores are reduced across those lanes with DPP steps.
+// Large grids use 256-thread workgroups with 32 columns per lane; grids
+// that would not fill the compute units use one-wave workgroups with 8
+// columns per lane, which spreads the rows over 4 D/32 times as many
+// compute units (each with its own LDS) and cuts the serial work per lane.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(
+template <int D, bool CAUSAL, int TPR, int NT>
+__global__ __launch_bounds__(NT) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
     int n_qtiles) {
-  constexpr int TPR = D / 32;          // lanes per query row
-  constexpr int ROWS = 256 / TPR;      // query rows per workgroup
+  constexpr int CPL = D / TPR;         // columns per lane
+  constexpr int ROWS = NT / TPR;       // query rows per workgroup
   constexpr int BC = 32;               // keys per LDS tile
   __shared__ float sK[BC * D];
   __shared__ float sV[BC * D];
@@ -32,23 +36,23 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
   const int row = qtile * ROWS + tid / TPR;
-  const int col0 = (tid % TPR) * 32;
+  const int col0 = (tid % TPR) * CPL;
   const int off = Skv - Sq;
 
   const float* Qh = Q + ((int64_t)bh * Sq) * D;
   const float* Kh = K + ((int64_t)(b * Hkv + hk) * Skv) * D;
   const float* Vh = V + ((int64_t)(b * Hkv + hk) * Skv) * D;
 
-  float q[32];
-  KahanSum o[32];   // compensated, like the normaliser
+  float q[CPL];
+  KahanSum o[CPL];   // compensated, like the normaliser
   const bool valid = row < Sq;
 #pragma unroll
-  for (int c = 0; c < 32; c += 4) {
+  for (int c = 0; c < CPL; c += 4) {
     f32x4 x = valid ? *(const f32x4*)(Qh + (int64_t)row * D + col0 + c) : f32x4{0, 0, 0, 0};
     q[c] = x[0]; q[c + 1] = x[1]; q[c + 2] = x[2]; q[c + 3] = x[3];
   }
 #pragma unroll
-  for (int c = 0; c < 32; ++c) o[c] = KahanSum{0.f, 0.f};
+  for (int c = 0; c < CPL; ++c) o[c] = KahanSum{0.f, 0.f};
   // Keys [row_lo, row_limit); a sliding window of `window` keys (causal
   // only, 0 = none) raises the lower end.
   const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
@@ -65,16 +69,30 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   KahanSum l{0.f, 0.f};
   for (int k0 = kv_begin; k0 < kv_end; k0 += BC) {
     __syncthreads();
-    for (int e = tid * 4; e < BC * D; e += 256 * 4) {
-      const int r = e / D, c = e % D;
-      const int key = k0 + r;
-      f32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (key < Skv) {
-        kx = *(const f32x4*)(Kh + (int64_t)key * D + c);
-        vx = *(const f32x4*)(Vh + (int64_t)key * D + c);
+    // The tile in groups of up to 8 16-byte chunks per lane and tensor, all
+    // loads of a group issued before its LDS stores (one memory round trip
+    // per group, not per chunk).
+    constexpr int NCH = BC * D / (NT * 4);   // chunks per lane and tensor
+    constexpr int GRP = NCH < 8 ? NCH : 8;
+#pragma unroll
+    for (int i0 = 0; i0 < NCH; i0 += GRP) {
+      f32x4 kx[GRP], vx[GRP];
+#pragma unroll
+      for (int i = 0; i < GRP; ++i) {
+        const int e = ((i0 + i) * NT + tid) * 4;
+        const int key = k0 + e / D, c = e % D;
+        kx[i] = vx[i] = f32x4{0, 0, 0, 0};
+        if (key < Skv) {
+          kx[i] = *(const f32x4*)(Kh + (int64_t)key * D + c);
+          vx[i] = *(const f32x4*)(Vh + (int64_t)key * D + c);
+        }
       }
-      *(f32x4*)(sK + r * D + c) = kx;
-      *(f32x4*)(sV + r * D + c) = vx;
+#pragma unroll
+      for (int i = 0; i < GRP; ++i) {
+        const int e = ((i0 + i) * NT + tid) * 4;
+        *(f32x4*)(sK + e) = kx[i];
+        *(f32x4*)(sV + e) = vx[i];
+      }
     }
     __syncthreads();
 
@@ -84,15 +102,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     for (int j = 0; j < BC; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 32; c += 4) {
+      for (int c = 0; c < CPL; c += 4) {
         f32x4 kx = *(const f32x4*)(sK + j * D + col0 + c);
         acc = fmaf(q[c], kx[0], acc);
         acc = fmaf(q[c + 1], kx[1], acc);
         acc = fmaf(q[c + 2], kx[2], acc);
         acc = fmaf(q[c + 3], kx[3], acc);
       }
-#pragma unroll
-      for (int w = 1; w < TPR; w <<= 1) acc += __shfl_xor(acc, w);
+      acc = group_reduce<TPR, false>(acc);
       float x = kNegInf;
       if (k0 + j < row_limit && k0 + j >= row_lo)
         x = brow ? fmaf(brow[k0 + j], kLog2e, acc * scale_log2) : acc * scale_log2;
@@ -104,15 +121,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     // The tile's terms are summed from zero, then added to the rescaled
     // running (l, o): one by one, terms far below a large running value
     // would round away over long sequences.
-    float lt = 0.f, ot[32];
+    float lt = 0.f, ot[CPL];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) ot[c] = 0.f;
+    for (int c = 0; c < CPL; ++c) ot[c] = 0.f;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
       const float p = fast_exp2(s[j] - msub);
       lt += p;
 #pragma unroll
-      for (int c = 0; c < 32; c += 4) {
+      for (int c = 0; c < CPL; c += 4) {
         f32x4 vx = *(const f32x4*)(sV + j * D + col0 + c);
         ot[c] = fmaf(p, vx[0], ot[c]);
         ot[c + 1] = fmaf(p, vx[1], ot[c + 1]);
@@ -123,7 +140,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     l.scale(alpha);
     l.add(lt);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
+    for (int c = 0; c < CPL; ++c) {
       o[c].scale(alpha);
       o[c].add(ot[c]);
     }
@@ -134,7 +151,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const float inv = lv > 0.f ? 1.f / lv : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   float* Oh = O + ((int64_t)bh * Sq + row) * D + col0;
 #pragma unroll
-  for (int c = 0; c < 32; c += 4) {
+  for (int c = 0; c < CPL; c += 4) {
     *(f32x4*)(Oh + c) = f32x4{o[c].value() * inv, o[c + 1].value() * inv,
                               o[c + 2].value() * inv, o[c + 3].value() * inv};
   }
@@ -172,6 +189,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 constexpr float kLazy = 8.f;
 constexpr float kLazyBound = 256.f;   // 2^kLazy
 
+// Keys per K/V tile.  d64 takes 64-key tiles: a 32-key tile gives each wave
+// only 8 products between barriers, and the wider tile (32 KB of LDS per
+// workgroup, as d128 with 32 keys) is 4-8 % faster on MI355X; d128 and d256
+// are fastest with 32 (the 64-key d128 tile costs a third workgroup per CU).
+// The bias path adds its values tile by tile for 32 keys.
+template <int D, bool BIAS>
+constexpr int kFwdKeys = (D == 64 && !BIAS) ? 64 : 32;
+
 template <int D, bool CAUSAL, int NW, bool WIN, bool BIAS>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -179,7 +204,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
     int n_qtiles) {
   constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
-  constexpr int BC = 32;         // keys per tile
+  constexpr int BC = kFwdKeys<D, BIAS>;   // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
@@ -435,18 +460,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
-  constexpr int ROWS = 256 / (D / 32);
+template <int D, bool CAUSAL, int TPR, int NT>
+static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
+  constexpr int ROWS = NT / TPR;
   const int n_qtiles = (a.Sq + ROWS - 1) / ROWS;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT>), dim3(n_qtiles * BH), dim3(NT), 0,
+                     a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
                      a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
+}
+
+// Fewer 256-thread workgroups than compute units: one-wave workgroups.
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
+  constexpr int ROWS = 256 / (D / 32);
+  const int64_t big = (int64_t)((a.Sq + ROWS - 1) / ROWS) * a.B * a.Hq;
+  if (big < device_cus()) return launch_fwd_f32_c<D, CAUSAL, D / 8, 64>(a);
+  return launch_fwd_f32_c<D, CAUSAL, D / 32, 256>(a);
 }
 
 // Waves per workgroup: every wave holds 32 query rows, and all waves of a

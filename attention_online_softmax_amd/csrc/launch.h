@@ -66,6 +66,16 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Compute units of the current device (256 if the query fails).
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
 // Records the caller's timing event for `slot` (2i before / 2i+1 after the
 // i-th kernel of the current entry point) if timing events are set.
 void timing_mark(hipStream_t stream, int slot);

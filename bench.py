@@ -5,8 +5,9 @@ One step = attn_fwd followed by attn_bwd on the training workload
 split-KV decode, which is timed in the same run on its own workload
 (bf16, B=8, Hq=32, Hkv=8, Skv=4096, d=128, 16 splits), as are the same
 decode over a paged cache (shuffled 64-key pages), the training step with
-a 512-key sliding window, the training step with an additive fp32 bias, and
-the 44k-token head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
+a 512-key sliding window, the training step with an additive fp32 bias, the
+fp32 128-token and bf16 transformer-block (S512 d64) forwards, and the
+44k-token head-dim-256 causal prefill.  Inputs are seeded synthetic tensors already
 resident in device memory; three input sets rotate so that no step reuses
 the previous step's data from the 256 MiB last-level cache.
 
@@ -17,7 +18,7 @@ timed with HIP events recorded around that kernel inside the timed region.
 `cpu_baseline` times the float64 oracle on a bounded sample on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill]
+                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill|small]
 """
 from __future__ import annotations
 
@@ -560,6 +561,58 @@ def measured_ceilings(stream):
             "spec_hbm_GB/s": PEAK_HBM_GBS, "spec_bf16_TFLOP/s": PEAK_BF16_TFLOPS}
 
 
+def bench_small(args, hev, stream, reps):
+    """The two small forward workloads: fp32 B1 H1 S128 d64 (non-causal) and the
+    bf16 causal transformer-block forward B4 H16 S512 d64.  Cold: a 512 MiB
+    fill runs before every call (outside the timed span), so the inputs come
+    from HBM, not the 256 MiB last-level cache; warm: calls back to back on
+    the same inputs.  Events bracket only the forward kernel."""
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import WORKLOADS, make_workload
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for key in ("fp32_small", "block_fwd"):
+        w = WORKLOADS[key]
+        s = {k: v.cuda() for k, v in make_workload(w).items()}
+        o = torch.empty_like(s["q"])
+        lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
+
+        def fwd(i):
+            aos.attn_fwd(s["q"], s["k"], s["v"], causal=w.causal, scale=w.scale, o=o, lse=lse)
+
+        def evict(i):
+            flush.fill_(i & 255)
+
+        fwd(0)
+        torch.cuda.synchronize()
+        res = {}
+        for tag, calls in (("cold", [("evict", evict), ("fwd", fwd)]), ("warm", [("fwd", fwd)])):
+            _, times, _ = run_calls(calls, {"evict": 0, "fwd": 1}, hev, reps, stream)
+            res[tag] = quantiles([t[0] for t in times["fwd"] if t[0] is not None])
+        es = 4 if w.dtype == "f32" else 2
+        flop = flops_fwd(w)
+        # Q, K, V read once; O and LSE written once
+        nbytes = (2.0 * w.B * w.Hq * w.Sq * w.d * es + 2.0 * w.B * w.Hkv * w.Skv * w.d * es
+                  + w.B * w.Hq * w.Sq * 4)
+        peak_f = (157.3 if w.dtype == "f32" else PEAK_BF16_TFLOPS) * 1e12
+        floor_us = max(flop / peak_f, nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        r = {"workload": f"{key}: {w.title}", "dtype": w.dtype,
+             "us_median": res["cold"]["median"] * 1e3, "us_p10": res["cold"]["p10"] * 1e3,
+             "us_p90": res["cold"]["p90"] * 1e3, "us_median_warm": res["warm"]["median"] * 1e3,
+             "FLOP": flop, "algorithmic_bytes": nbytes,
+             "roofline_floor_us": floor_us,
+             "roofline_bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flop / peak_f else "mfma",
+             "frac_of_roofline": floor_us / (res["cold"]["median"] * 1e3)}
+        if w.dtype == "bf16":
+            r["TFLOP/s"] = flop / (res["cold"]["median"] * 1e-3) / 1e12
+            r["frac_of_bf16_peak"] = r["TFLOP/s"] / PEAK_BF16_TFLOPS
+            r["GB/s"] = nbytes / (res["cold"]["median"] * 1e-3) / 1e9
+            r["frac_of_8TBs"] = r["GB/s"] / PEAK_HBM_GBS
+        out[key] = r
+    return out
+
+
 def bench_prefill(args, hev, stream, reps):
     import torch
     import attention_online_softmax_amd as aos
@@ -591,7 +644,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill"],
+    ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill", "small"],
                     default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -614,6 +667,9 @@ def main():
         return
     if args.only == "paged_decode":
         print(json.dumps(bench_decode_paged(args, hev, stream, args.steps)), flush=True)
+        return
+    if args.only == "small":
+        print(json.dumps(bench_small(args, hev, stream, args.steps)), flush=True)
         return
     if args.only == "prefill":
         print(json.dumps(bench_prefill(args, hev, stream, args.steps)), flush=True)
@@ -640,6 +696,10 @@ def main():
         extras["fused_bwd"] = bench_fused_bwd(args, hev, stream, max(args.steps, 20))
         print(f"[bench] backward two-kernel {extras['fused_bwd']['two_kernel_us']:.1f} us, "
               f"fused {extras['fused_bwd']['fused_us']:.1f} us", file=sys.stderr, flush=True)
+        extras["small_fwd"] = bench_small(args, hev, stream, max(args.steps, 50))
+        print(f"[bench] fp32 S128 fwd {extras['small_fwd']['fp32_small']['us_median']:.1f} us, "
+              f"block fwd {extras['small_fwd']['block_fwd']['us_median']:.1f} us",
+              file=sys.stderr, flush=True)
         extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
         print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",
               file=sys.stderr, flush=True)
