@@ -134,3 +134,43 @@ def test_fwd_errors_raise():
     dev, _ = inputs(1, 2, 2, 9, 8, 64, "bf16", 5)
     with pytest.raises(aos.AttnError):
         aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+
+
+# fp32 grids of at least 256 workgroups of 256 threads run the 256-thread
+# configuration of the fp32 kernel (32 columns per lane); smaller grids,
+# as in CASES above, the one-wave configuration (8 columns per lane).
+F32_LARGE = [
+    (2, 64, 16, 200, 250, 64, True),    # 2 x 64 heads x 2 tiles of 128 rows
+    (1, 40, 8, 400, 300, 128, False),   # 40 heads x 7 tiles of 64 rows
+    (1, 8, 2, 1100, 1100, 256, True),   # 8 heads x 35 tiles of 32 rows
+]
+
+
+@pytest.mark.parametrize("case", F32_LARGE, ids=lambda c: "B{}_Hq{}_Hkv{}_Sq{}_Skv{}_d{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_fwd_f32_large_grid(case):
+    B, Hq, Hkv, Sq, Skv, d, causal = case
+    dev, ref = inputs(B, Hq, Hkv, Sq, Skv, d, "f32", 300 + sum(case[:6]))
+    scale = 1 / math.sqrt(d)
+    note(f"fwd f32 large grid {case}")
+    o, lse = run_fwd(dev, causal, scale)
+    O, L = oracle.attention_ref(ref["q"], ref["k"], ref["v"], causal, scale)
+    assert_close(to_f64(o), O, TOL_O["f32"], "O")
+    assert_close(lse.cpu().numpy(), L, TOL_LSE["f32"], "LSE")
+
+
+def test_fwd_f32_large_grid_window_bias():
+    """The 256-thread fp32 configuration with a sliding window and a
+    per-batch additive bias (rows with no allowed key included)."""
+    from tests.test_gpu_bias import check_fwd, make_bias
+    B, Hq, Hkv, Sq, Skv, d, W = 2, 64, 64, 130, 132, 64, 50
+    dev, ref = inputs(B, Hq, Hkv, Sq, Skv, d, "f32", 777)
+    bias = make_bias("head1", B, Hq, Sq, Skv, 778)
+    scale = 1 / math.sqrt(d)
+    note("fwd f32 large grid window + bias")
+    o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True, scale=scale, window=W,
+                          bias=bias.cuda())
+    torch.cuda.synchronize()
+    bf = np.broadcast_to(bias.numpy().astype(np.float64), (B, Hq, Sq, Skv))
+    O, L = oracle.attention_ref(ref["q"], ref["k"], ref["v"], True, scale, window=W, bias=bf)
+    check_fwd(o, lse, O, L, "f32", "f32 large grid window + bias")
