@@ -219,11 +219,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x % BH;
-  const int t = blockIdx.x / BH;
+  // Work item: query tile t (heaviest first when causal) of key/value head
+  // hk of batch b, ranked r = t * B * Hkv + b * Hkv + hk, and one of its G
+  // query heads.  Workgroup ids congruent mod 8 run on the same XCD, so the
+  // G query heads of item r take ids 8 (G (r / 8) + j) + r % 8, j < G: they
+  // read the item's key/value tiles through one L2.
+  const int G = Hq / Hkv;
+  const int BHk = BH / G;   // B * Hkv
+  const int qq = blockIdx.x >> 3;
+  const int r = (qq / G) * 8 + (blockIdx.x & 7);
+  if (r >= n_qtiles * BHk) return;   // padding of the last group of 8 items
+  const int t = r / BHk;
+  const int b = (r % BHk) / Hkv, hk = (r % BHk) % Hkv;
+  const int h = hk * G + qq % G;
+  const int bh = b * Hq + h;
   const int qtile = CAUSAL ? (n_qtiles - 1 - t) : t;
-  const int b = bh / Hq, h = bh % Hq;
-  const int hk = h / (Hq / Hkv);
   const int off = Skv - Sq;
   const int q0 = qtile * BR;
   const int row = q0 + wave * 32 + n;
@@ -499,7 +509,11 @@ static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
   const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN, BIAS>), dim3(n_qtiles * BH),
+  // Items of (query tile, batch, key/value head) in groups of 8, one
+  // workgroup per query head of each (see the kernel's work mapping).
+  const int items = n_qtiles * a.B * a.Hkv;
+  const int grid = (items + 7) / 8 * 8 * (a.Hq / a.Hkv);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN, BIAS>), dim3(grid),
                      dim3(64 * NW), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
                      a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
