@@ -12,31 +12,40 @@ namespace attn {
 // float32 path: plain VALU arithmetic in fp32 end to end.
 // TPR consecutive lanes share one query row, each owning D/TPR of its
 // columns of q and o; scores are reduced across those lanes with DPP steps.
-// Large grids use 256-thread workgroups with 32 columns per lane; grids
-// that would not fill the compute units use one-wave workgroups with 8
-// columns per lane, which spreads the rows over 4 D/32 times as many
-// compute units (each with its own LDS) and cuts the serial work per lane.
+// Large grids use 256-thread workgroups with 32 columns per lane (KW = 1:
+// the four waves hold different rows and share every K/V tile).  Grids that
+// would not fill the compute units use 8 columns per lane, which spreads
+// the rows over 4 D/32 times as many workgroups, and KW = 4: the four waves
+// of a workgroup hold the same rows and take every fourth key tile each,
+// through K/V buffers of their own, and their states (m, l, o) are merged
+// by the monoid at the end.  That cuts the serial VALU work per row by 4.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int TPR, int NT>
+template <int D, bool CAUSAL, int TPR, int NT, int KW>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
     int n_qtiles) {
+  static_assert(KW == 1 || NT == 64 * KW, "KW > 1: one wave per key share");
   constexpr int CPL = D / TPR;         // columns per lane
-  constexpr int ROWS = NT / TPR;       // query rows per workgroup
-  constexpr int BC = 32;               // keys per LDS tile
-  __shared__ float sK[BC * D];
-  __shared__ float sV[BC * D];
+  constexpr int NTR = NT / KW;         // threads that share a K/V tile
+  constexpr int ROWS = NTR / TPR;      // query rows per workgroup
+  constexpr int BC = (KW > 1 && D >= 256) ? 16 : 32;   // keys per LDS tile
+  __shared__ float sK[KW * BC * D];
+  __shared__ float sV[KW * BC * D];
 
   const int tid = threadIdx.x;
+  const int wk = KW > 1 ? tid / 64 : 0;     // key share of this wave
+  const int ltid = KW > 1 ? tid % 64 : tid;
+  float* const tK = sK + wk * BC * D;
+  float* const tV = sV + wk * BC * D;
   const int bh = blockIdx.x % BH;
   const int t = blockIdx.x / BH;
   const int qtile = CAUSAL ? (n_qtiles - 1 - t) : t;
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
-  const int row = qtile * ROWS + tid / TPR;
-  const int col0 = (tid % TPR) * CPL;
+  const int row = qtile * ROWS + ltid / TPR;
+  const int col0 = (ltid % TPR) * CPL;
   const int off = Skv - Sq;
 
   const float* Qh = Q + ((int64_t)bh * Sq) * D;
@@ -67,19 +76,21 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
 
   float m = kNegInf;
   KahanSum l{0.f, 0.f};
-  for (int k0 = kv_begin; k0 < kv_end; k0 += BC) {
-    __syncthreads();
+  // KW > 1: wave wk takes tiles kv_begin + wk BC, + KW BC, ...; its LDS
+  // accesses are in program order, so its own buffers need no barrier.
+  for (int k0 = kv_begin + wk * BC; k0 < kv_end; k0 += KW * BC) {
+    if (KW == 1) __syncthreads();
     // The tile in groups of up to 8 16-byte chunks per lane and tensor, all
     // loads of a group issued before its LDS stores (one memory round trip
     // per group, not per chunk).
-    constexpr int NCH = BC * D / (NT * 4);   // chunks per lane and tensor
+    constexpr int NCH = BC * D / (NTR * 4);   // chunks per lane and tensor
     constexpr int GRP = NCH < 8 ? NCH : 8;
 #pragma unroll
     for (int i0 = 0; i0 < NCH; i0 += GRP) {
       f32x4 kx[GRP], vx[GRP];
 #pragma unroll
       for (int i = 0; i < GRP; ++i) {
-        const int e = ((i0 + i) * NT + tid) * 4;
+        const int e = ((i0 + i) * NTR + ltid) * 4;
         const int key = k0 + e / D, c = e % D;
         kx[i] = vx[i] = f32x4{0, 0, 0, 0};
         if (key < Skv) {
@@ -89,12 +100,12 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int i = 0; i < GRP; ++i) {
-        const int e = ((i0 + i) * NT + tid) * 4;
-        *(f32x4*)(sK + e) = kx[i];
-        *(f32x4*)(sV + e) = vx[i];
+        const int e = ((i0 + i) * NTR + ltid) * 4;
+        *(f32x4*)(tK + e) = kx[i];
+        *(f32x4*)(tV + e) = vx[i];
       }
     }
-    __syncthreads();
+    if (KW == 1) __syncthreads();
 
     float s[BC];
     float mx = m;
@@ -103,7 +114,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; c += 4) {
-        f32x4 kx = *(const f32x4*)(sK + j * D + col0 + c);
+        f32x4 kx = *(const f32x4*)(tK + j * D + col0 + c);
         acc = fmaf(q[c], kx[0], acc);
         acc = fmaf(q[c + 1], kx[1], acc);
         acc = fmaf(q[c + 2], kx[2], acc);
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
       lt += p;
 #pragma unroll
       for (int c = 0; c < CPL; c += 4) {
-        f32x4 vx = *(const f32x4*)(sV + j * D + col0 + c);
+        f32x4 vx = *(const f32x4*)(tV + j * D + col0 + c);
         ot[c] = fmaf(p, vx[0], ot[c]);
         ot[c + 1] = fmaf(p, vx[1], ot[c + 1]);
         ot[c + 2] = fmaf(p, vx[2], ot[c + 2]);
@@ -146,6 +157,40 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
     }
     m = mx;
   }
+  if constexpr (KW > 1) {
+    // Merge the KW states of each lane (same row and columns in every
+    // wave) in wave order: M = max m_w, weights 2^(m_w - M) (0 for a wave
+    // that saw no key), l and o summed with those weights.
+    constexpr int NV = CPL + 2;
+    __syncthreads();   // every wave has left its tile loop
+    if (wk > 0) {
+      sK[((wk - 1) * NV + 0) * 64 + ltid] = m;
+      sK[((wk - 1) * NV + 1) * 64 + ltid] = l.value();
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) sK[((wk - 1) * NV + 2 + c) * 64 + ltid] = o[c].value();
+    }
+    __syncthreads();
+    if (wk > 0) return;
+    float M = m;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) M = fmaxf(M, sK[((w - 1) * NV) * 64 + ltid]);
+    const float f0 = m == kNegInf ? 0.f : fast_exp2(m - M);
+    float lm = l.value() * f0, om[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) om[c] = o[c].value() * f0;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      const float mw = sK[((w - 1) * NV) * 64 + ltid];
+      const float fw = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+      lm = fmaf(sK[((w - 1) * NV + 1) * 64 + ltid], fw, lm);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) om[c] = fmaf(sK[((w - 1) * NV + 2 + c) * 64 + ltid], fw, om[c]);
+    }
+    m = M;
+    l = KahanSum{lm, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] = KahanSum{om[c], 0.f};
+  }
   if (!valid) return;
   const float lv = l.value();
   const float inv = lv > 0.f ? 1.f / lv : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
@@ -155,7 +200,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
     *(f32x4*)(Oh + c) = f32x4{o[c].value() * inv, o[c + 1].value() * inv,
                               o[c + 2].value() * inv, o[c + 3].value() * inv};
   }
-  if (LSE && (tid % TPR) == 0) LSE[(int64_t)bh * Sq + row] = (m + fast_log2(lv)) * kLn2;
+  if (LSE && (ltid % TPR) == 0) LSE[(int64_t)bh * Sq + row] = (m + fast_log2(lv)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -470,13 +515,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int TPR, int NT>
+template <int D, bool CAUSAL, int TPR, int NT, int KW>
 static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
-  constexpr int ROWS = NT / TPR;
+  constexpr int ROWS = NT / KW / TPR;
   const int n_qtiles = (a.Sq + ROWS - 1) / ROWS;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT>), dim3(n_qtiles * BH), dim3(NT), 0,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT, KW>), dim3(n_qtiles * BH), dim3(NT), 0,
                      a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
@@ -485,13 +530,14 @@ static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
   return hipGetLastError();
 }
 
-// Fewer 256-thread workgroups than compute units: one-wave workgroups.
+// Fewer 256-thread workgroups than compute units: 8 columns per lane and
+// the keys split over the four waves of each workgroup.
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   constexpr int ROWS = 256 / (D / 32);
   const int64_t big = (int64_t)((a.Sq + ROWS - 1) / ROWS) * a.B * a.Hq;
-  if (big < device_cus()) return launch_fwd_f32_c<D, CAUSAL, D / 8, 64>(a);
-  return launch_fwd_f32_c<D, CAUSAL, D / 32, 256>(a);
+  if (big < device_cus()) return launch_fwd_f32_c<D, CAUSAL, D / 8, 256, 4>(a);
+  return launch_fwd_f32_c<D, CAUSAL, D / 32, 256, 1>(a);
 }
 
 // Waves per workgroup: every wave holds 32 query rows, and all waves of a
