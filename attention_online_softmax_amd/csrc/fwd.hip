@@ -217,11 +217,11 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
 // V tile through LDS transpose reads.  The accumulator O^T is again indexed
 // by the lane's query, so rescaling by alpha is a per-lane scalar.
 //
-// K/V tiles of 32 keys go from HBM straight into LDS with buffer loads to
-// LDS (no staging registers), double-buffered: tile j+1 is requested when
-// tile j's loop body starts.  Tiles are dense [32][D] with 16-byte
-// chunks XOR-swizzled per row (tile_swz) so that the K row reads and the V
-// transpose reads are free of bank conflicts.
+// K/V tiles of BC keys (32; 64 at d64, see kFwdKeys) go from HBM straight
+// into LDS with buffer loads to LDS (no staging registers), double-buffered:
+// tile j+1 is requested when tile j's loop body starts.  Tiles are dense
+// [BC][D] with 16-byte chunks XOR-swizzled per row (tile_swz) so that the K
+// row reads and the V transpose reads are free of bank conflicts.
 //
 // Normalisation reference: the exponentials are taken relative to a per-row
 // reference m_ref that only advances when a tile's probabilities against it
