@@ -284,6 +284,20 @@ def bench_fwd_bwd(args, hev, stream):
 
     calls = [("fwd", fwd), ("bwd", bwd)]
     nk = {"fwd": 1, "bwd": 2}
+    # Cold start, kept apart from the kernel times: the first call of each
+    # entry point in the process (host wall time to completion, and GPU time
+    # between events around it; includes loading the kernels' code).
+    torch.cuda.synchronize()
+    first = {}
+    for name, fn in calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        fn(0)
+        e1.record()
+        torch.cuda.synchronize()
+        first[name] = {"host_wall_ms": (time.perf_counter() - t0) * 1e3,
+                       "gpu_ms": e0.elapsed_time(e1)}
     for i in range(args.warmup):
         fwd(i)
         bwd(i)
@@ -312,6 +326,7 @@ def bench_fwd_bwd(args, hev, stream):
         "fwd": {"ms": fwd_ms, "TFLOP/s": flop_fwd / (fwd_ms * 1e-3) / 1e12},
         "bwd": {"ms": bwd_ms, "TFLOP/s": 2.5 * flop_fwd / (bwd_ms * 1e-3) / 1e12},
         "kernels": ks,
+        "first_call": first,
         "dominant": dom,
         "dominant_timed": dom_stats,
     }
@@ -740,6 +755,7 @@ def main():
         "fwd": r["fwd"],
         "bwd": r["bwd"],
         "kernels": ks,
+        "first_call": r["first_call"],
     }
     line.update(extras)
     if not args.no_extras and args.only is None:
