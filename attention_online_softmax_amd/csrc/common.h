@@ -182,11 +182,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Cache policy of a load to LDS: kCacheDefault, or kCacheStream (the
+// non-temporal hint) for data read once, such as the key/value cache of a
+// decode step, which then does not displace lines that are reused.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+
 // This wave's share of the transfer of rows r0 .. r0+ROWS-1 of a row-major
 // [*, D] bf16 matrix (rows at or beyond rlimit read row rlimit-1 instead)
 // into the swizzled tile `dst`.  Each global_load_lds moves 64 chunks of 16
 // bytes: lane l of block blk fills physical chunk blk*64 + l.
-template <int D, int ROWS, int NWAVES>
+template <int D, int ROWS, int NWAVES, int CPOL = kCacheDefault>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int r0, int rlimit,
                                          int wave, int lane) {
   constexpr int CPR = D / 8;
@@ -204,7 +210,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
       const int lc = (pos % CPR) ^ tile_swz<D>(r);
       __builtin_amdgcn_global_load_lds((const void*)(base + (r * D + lc * 8)),
                                        (__attribute__((address_space(3))) void*)(dst + blk * 512),
-                                       16, 0, 0);
+                                       16, 0, CPOL);
     }
   } else {
 #pragma unroll
@@ -216,7 +222,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, uint16_t* dst, int
       const int row = min(r0 + r, rlimit - 1);
       __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * D + lc * 8),
                                        (__attribute__((address_space(3))) void*)(dst + blk * 512),
-                                       16, 0, 0);
+                                       16, 0, CPOL);
     }
   }
 }
@@ -252,6 +258,7 @@ struct TileDma {
     }
   }
   // Rows r0 .. r0+ROWS-1 of the [rows, D] bf16 matrix at `src` into `dst`.
+  template <int CPOL = kCacheDefault>
   __device__ __forceinline__ void load(const uint16_t* src, int rows, uint16_t* dst, int r0,
                                        int wave) const {
     const rsrc_t rs = make_rsrc(src, (uint32_t)rows * D * 2);
@@ -263,7 +270,7 @@ struct TileDma {
       const int vo = voff[j];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(dst + (j * NWAVES + wave) * 512), 16, vo,
-          soff, 0, 0);
+          soff, 0, CPOL);
     }
   }
 };

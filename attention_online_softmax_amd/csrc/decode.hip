@@ -426,13 +426,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
       const bool ok = p >= 0 && p < pg.n_pages;
       const int64_t base = ((int64_t)(ok ? p : 0) * Hkv + x.hk) * pg.page_size * D;
       const int r0 = tile_of(x, t) * TK % pg.page_size;
-      pdma.load(K + base, ok ? pg.page_size : 0, dK, r0, 0);
-      pdma.load(V + base, ok ? pg.page_size : 0, dV, r0, 0);
+      // The cache is read once per step: non-temporal loads.
+      pdma.template load<kCacheStream>(K + base, ok ? pg.page_size : 0, dK, r0, 0);
+      pdma.template load<kCacheStream>(V + base, ok ? pg.page_size : 0, dV, r0, 0);
     } else {
       const int64_t base = (int64_t)(x.b * Hkv + x.hk) * Skv * D;
       const int r0 = tile_of(x, t) * TK;
-      dma_tile<D, TK, 1>(K + base, dK, r0, Skv, 0, lane);
-      dma_tile<D, TK, 1>(V + base, dV, r0, Skv, 0, lane);
+      dma_tile<D, TK, 1, kCacheStream>(K + base, dK, r0, Skv, 0, lane);
+      dma_tile<D, TK, 1, kCacheStream>(V + base, dV, r0, Skv, 0, lane);
     }
   };
   // Raw query rows of the unit's heads (lanes past the group's heads load a

@@ -534,16 +534,16 @@ def measured_ceilings(stream):
     from attention_online_softmax_amd.build import CEIL_LIB
     L = ctypes.CDLL(CEIL_LIB)
     L.ceil_read_run.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                ctypes.c_void_p]
+                                ctypes.c_int, ctypes.c_void_p]
     L.ceil_mfma_run.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     st = ctypes.c_void_p(stream.cuda_stream)
     nbytes, blocks = 1 << 30, 1024
     bufs = [torch.ones(nbytes // 4, device="cuda", dtype=torch.int32) for _ in range(3)]
     out = torch.empty(blocks * 256, device="cuda", dtype=torch.float32)
 
-    def read(i):
+    def read(i, nt=0):
         rc = L.ceil_read_run(ctypes.c_void_p(bufs[i % 3].data_ptr()), nbytes,
-                             ctypes.c_void_p(out.data_ptr()), blocks, st)
+                             ctypes.c_void_p(out.data_ptr()), blocks, nt, st)
         if rc:
             raise RuntimeError(f"ceil_read_run: hip error {rc}")
 
@@ -559,7 +559,9 @@ def measured_ceilings(stream):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
 
-    read_gbs = nbytes / timed(read, 12) / 1e9
+    read_default = nbytes / timed(read, 12) / 1e9
+    read_nt = nbytes / timed(lambda i: read(i, 1), 12) / 1e9
+    read_gbs = max(read_default, read_nt)
     del bufs
     mblocks, iters = 512, 4000
 
@@ -570,7 +572,9 @@ def measured_ceilings(stream):
 
     mfma_tf = mblocks * 4 * iters * 16 * 32768.0 / timed(mf, 5) / 1e12
     return {"hbm_read_GB/s": read_gbs,
-            "hbm_read_kind": "grid-stride 16-byte loads over 1 GiB, 3 rotating buffers",
+            "hbm_read_kind": "grid-stride 16-byte loads over 1 GiB, 3 rotating buffers; "
+                             "the faster of plain and non-temporal loads",
+            "hbm_read_plain_GB/s": read_default, "hbm_read_nontemporal_GB/s": read_nt,
             "bf16_mfma_TFLOP/s": mfma_tf,
             "bf16_mfma_kind": "32x32x16 bf16 MFMAs from registers, 4 chains, 2 waves/SIMD",
             "spec_hbm_GB/s": PEAK_HBM_GBS, "spec_bf16_TFLOP/s": PEAK_BF16_TFLOPS}
