@@ -72,9 +72,10 @@ __device__ __forceinline__ void decode_dma(const T* src, T* dst, int L, int wave
     const int blk = j * 4 + wave;
     const int pos = blk * 64 + lane;                  // chunk index within the stage
     const int r = min(pos / C::CPR, L - 1);           // rows past the chunk end repeat
+    // The cache is read once per step: non-temporal loads.
     __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)r * D + (pos % C::CPR) * C::E),
                                      (__attribute__((address_space(3))) void*)(dst + blk * 1024 / (int)sizeof(T)),
-                                     16, 0, 0);
+                                     16, 0, kCacheStream);
   }
 }
 
