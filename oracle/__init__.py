@@ -5,7 +5,6 @@ benchmark's CPU-baseline leg, never by the HIP library or its binding.
 """
 from .attention import (  # noqa: F401
     NEG_INF,
-    allowed_keys,
     attention_bwd_ref,
     attention_monoid,
     attention_ref,

@@ -80,20 +80,6 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, Sq, Skv, d, v.shape[3]
 
 
-def allowed_keys(i, Sq, Skv, causal):
-    """Number of allowed keys for query row i (keys 0 .. n-1 are allowed).
-
-    Mask C of the first display equation, causal pattern, bottom-right
-    aligned: key j is allowed iff j <= i + (Skv - Sq).
-    """
-    if not causal:
-        return Skv
-    n = i + (Skv - Sq) + 1
-    if n < 1:
-        raise ValueError("a query row has no allowed key (causal with Sq > Skv)")
-    return min(n, Skv)
-
-
 def mask_matrix(rows, Sq, Skv, causal, window=0):
     """Additive mask C restricted to the given query rows: 0 or -inf.  With
     window W > 0 (causal only), keys more than W - 1 before the diagonal are

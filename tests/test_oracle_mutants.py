@@ -73,6 +73,21 @@ MUTANTS = [
     ("bias dropped", "        s = s + bias[b, hq][rows]", "        s = s + 0 * bias[b, hq][rows]", 0),
     ("bias rows reversed", "        s = s + bias[b, hq][rows]",
      "        s = s + bias[b, hq][::-1][rows]", 0),
+    ("identity normaliser one", "return np.full(n, NEG_INF), np.zeros(n), np.zeros((n, dv))",
+     "return np.full(n, NEG_INF), np.ones(n), np.zeros((n, dv))", 0),
+    ("monoid pairwise drops odd block", "                    if len(states) % 2:\n"
+     "                        nxt.append(states[-1])",
+     "                    if len(states) % 2 and False:\n"
+     "                        nxt.append(states[-1])", 0),
+    ("monoid left fold skips first block", "                for st in states:\n"
+     "                    acc = merge(acc, st)",
+     "                for st in states[1:]:\n"
+     "                    acc = merge(acc, st)", 0),
+    ("decode combine drops last split", "    for sp in range(n_splits):\n        st = merge(st,",
+     "    for sp in range(n_splits - 1):\n        st = merge(st,", 0),
+    ("decode ref keys and values swapped",
+     "return decode_combine(*decode_partials(q, k, v, scale, n_splits))",
+     "return decode_combine(*decode_partials(q, v, k, scale, n_splits))", 0),
     ("bias by key head", "        s = s + bias[b, hq][rows]", "        s = s + bias[b, hq // g][rows]",
      0),
 ]
