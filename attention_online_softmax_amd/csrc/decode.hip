@@ -447,8 +447,12 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NDC; ++c) qr[c] = *(const u32x4*)(qp + c * 16);
   };
+  // A zero scale makes every score 0: the query rows are replaced by zeros
+  // and the scale by 1 (the same exact scores; keys past the end stay -inf,
+  // where -inf times a zero scale would be NaN).
+  const bool zero_scale = scale_log2 == 0.f;
   auto q_keep = [&](const Unit& x) {
-    return (n < min(HC, G - x.hc * HC)) ? 0xffffffffu : 0u;
+    return (n < min(HC, G - x.hc * HC) && !zero_scale) ? 0xffffffffu : 0u;
   };
   auto write_state = [&](const Unit& x, float m, float lpart, const f32x16* oacc) {
     const int nh = min(HC, G - x.hc * HC);
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma_kernel(
   if (u >= n_units) return;
 
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float c2 = fabsf(scale_log2);
+  const float c2 = zero_scale ? 1.f : fabsf(scale_log2);
   int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);

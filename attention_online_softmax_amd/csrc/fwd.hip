@@ -305,9 +305,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   if (CAUSAL) t_mask = min(t_mask, (q0 + off + 1) / BC);
 
   // A negative scale is applied as |scale| on -Q (bf16 negation is exact),
-  // so the maximum can be taken on raw scores and scaled afterwards.
+  // so the maximum can be taken on raw scores and scaled afterwards.  A zero
+  // scale makes every score 0: Q is replaced by zeros and the scale by 1,
+  // which gives the same exact scores while masked ones stay -inf (a raw
+  // -inf times a zero scale would be NaN).
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float c2 = fabsf(scale_log2);
+  const uint32_t qkeep = scale_log2 == 0.f ? 0u : 0xffffffffu;
+  const float c2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
   // With an additive bias the scores are taken to the log2 domain before the
   // softmax (s c2 + bias log2(e)), which then works with unit scale.
   const float c2s = BIAS ? 1.f : c2;
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < NDC; ++c) {
     qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
-    qreg[c] ^= qsign;
+    qreg[c] = (qreg[c] ^ qsign) & qkeep;
   }
   dma.load(Kh, Skv, sK0, j0 * BC, wave);
   dma.load(Vh, Skv, sV0, j0 * BC, wave);

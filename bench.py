@@ -155,16 +155,33 @@ def blas_threads():
     return os.cpu_count() or 1
 
 
-def cpu_baseline(w, cpu_inputs, budget_s=15.0):
+# Tolerances of the parity check on the timed inputs (max-abs against the
+# float64 oracle), as in the parity tests.
+TOL = {"O_bf16": 2e-2, "O_f32": 1e-5, "LSE_bf16": 1e-3, "LSE_f32": 1e-5, "grad": 5e-2}
+PARITY_SLICES = 8   # (batch, head) slices of the timed step compared with the oracle
+
+
+def _max_abs(a, b):
+    import numpy as np
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        return float("inf")
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def cpu_baseline(w, cpu_inputs, gpu_out=None, budget_s=15.0):
     """Time the oracle as it stands on whole heads of the same inputs (every
     (batch, head) in turn, starting over if all are done) until about
-    budget_s seconds have passed; report algorithmic TFLOP/s."""
+    budget_s seconds have passed; report algorithmic TFLOP/s.  The oracle's
+    results for the first PARITY_SLICES slices are then compared (outside
+    the timing) with the GPU's outputs of the timed step on those slices."""
     import oracle
     from attention_online_softmax_amd.inputs import to_f64
     q, k, v, do = (cpu_inputs[n] for n in ("q", "k", "v", "do"))
     G = w.Hq // w.Hkv
     pairs = w.pairs_per_head()
     done, flop = 0, 0.0
+    kept = []
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         i = done % (w.B * w.Hq)
@@ -174,17 +191,121 @@ def cpu_baseline(w, cpu_inputs, budget_s=15.0):
         kk = to_f64(k[b:b + 1, kh:kh + 1])
         vv = to_f64(v[b:b + 1, kh:kh + 1])
         dd = to_f64(do[b:b + 1, h:h + 1])
-        _, lse = oracle.attention_ref(qq, kk, vv, w.causal, w.scale)
-        oracle.attention_bwd_ref(qq, kk, vv, dd, w.causal, w.scale, lse=lse)
+        O, lse = oracle.attention_ref(qq, kk, vv, w.causal, w.scale)
+        grads = oracle.attention_bwd_ref(qq, kk, vv, dd, w.causal, w.scale, lse=lse)
+        if done < PARITY_SLICES and G == 1:
+            kept.append((b, h, O, lse, grads[:3]))
         done += 1
         flop += 14.0 * w.d * pairs
     dt = time.perf_counter() - t0
+    parity = None
+    if gpu_out is not None and kept:
+        err = {"O": 0.0, "LSE": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0}
+        for b, h, O, lse, (rq, rk, rv) in kept:
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            for name, ref in (("O", O), ("dQ", rq), ("dK", rk), ("dV", rv)):
+                key = {"O": "o", "dQ": "dq", "dK": "dk", "dV": "dv"}[name]
+                err[name] = max(err[name], _max_abs(to_f64(gpu_out[key][sl]), ref))
+            err["LSE"] = max(err["LSE"], _max_abs(gpu_out["lse"][sl].numpy(), lse))
+        tol = {"O": TOL["O_bf16"], "LSE": TOL["LSE_bf16"], "dQ": TOL["grad"], "dK": TOL["grad"],
+               "dV": TOL["grad"]}
+        parity = {"slices": [[b, h] for b, h, *_ in kept], "max_abs": err, "tol": tol,
+                  "pass": all(err[x] <= tol[x] for x in err)}
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "cores_meaning": "BLAS threads of numpy's matrix products (the element-wise "
+                             "exp runs on one thread)",
+            "host_affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"float64 oracle forward+backward on {done} (batch, head) slices of the "
                       f"same inputs ({w.B * w.Hq} distinct, taken in order), full S={w.Sq}, "
                       f"{dt:.1f} s",
-            "seconds": dt}
+            "seconds": dt, "parity_on_timed_inputs": parity}
+
+
+def parity_extras(extras, probes):
+    """The other timed workloads' outputs (first input set) against the
+    oracle: the decode and paged decode in full, the small forwards in full,
+    the 44k prefill on 16 rows of every head (first 8 and last 8)."""
+    import numpy as np
+    import oracle
+    from attention_online_softmax_amd.inputs import to_f64
+    out = {}
+    if "decode" in probes:
+        w, cpu, o, lse = probes["decode"]
+        O, L = oracle.decode_ref(to_f64(cpu["q"]), to_f64(cpu["k"]), to_f64(cpu["v"]), w.scale,
+                                 w.n_splits)
+        out["decode"] = {"O": _max_abs(to_f64(o), O), "LSE": _max_abs(lse.numpy(), L),
+                         "tol": {"O": TOL["O_bf16"], "LSE": TOL["LSE_bf16"]}}
+    if "paged_decode" in probes:
+        cpu, scale, o, lse = probes["paged_decode"]
+        ref = {k: (to_f64(v) if v.is_floating_point() else v.numpy()) for k, v in cpu.items()}
+        O, L = oracle.decode_paged_ref(ref["q"], ref["k_pages"], ref["v_pages"], ref["block_table"],
+                                       ref["seq_lens"], scale)
+        out["paged_decode"] = {"O": _max_abs(to_f64(o), O), "LSE": _max_abs(lse.numpy(), L),
+                               "tol": {"O": TOL["O_bf16"], "LSE": TOL["LSE_bf16"]}}
+    for key in ("fp32_small", "block_fwd"):
+        if key in probes:
+            w, cpu, o, lse = probes[key]
+            O, L = oracle.attention_ref(to_f64(cpu["q"]), to_f64(cpu["k"]), to_f64(cpu["v"]),
+                                        w.causal, w.scale)
+            out[key] = {"O": _max_abs(to_f64(o), O), "LSE": _max_abs(lse.numpy(), L),
+                        "tol": {"O": TOL[f"O_{w.dtype}"], "LSE": TOL[f"LSE_{w.dtype}"]}}
+    if "long_prefill" in probes:
+        w, cpu, rows, o, lse = probes["long_prefill"]
+        O, L = oracle.attention_ref(to_f64(cpu["q"]), to_f64(cpu["k"]), to_f64(cpu["v"]), w.causal,
+                                    w.scale, rows=np.asarray(rows))
+        out["long_prefill"] = {"rows_per_head": len(rows), "O": _max_abs(to_f64(o), O),
+                               "LSE": _max_abs(lse.numpy(), L),
+                               "tol": {"O": TOL["O_bf16"], "LSE": TOL["LSE_bf16"]}}
+    for r in out.values():
+        r["pass"] = all(r[x] <= r["tol"][x] for x in r["tol"])
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def run_conditions():
+    """What the numbers depend on besides the code: device, driver and
+    toolchain versions, the build flags, the library that was timed and the
+    host cores ("Compilers and Kernels", section "Operating the
+    compiler-kernel boundary": pin architecture, runtime, toolchain and
+    flags)."""
+    import subprocess
+    import torch
+    from attention_online_softmax_amd import build as B
+    from attention_online_softmax_amd.binding import LIB_PATH
+    props = torch.cuda.get_device_properties(0)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    try:
+        with open(os.path.join(rocm, ".info", "version")) as f:
+            rocm_version = f.read().strip()
+    except OSError:
+        rocm_version = None
+    try:
+        r = subprocess.run([B.hipcc(), "--version"], capture_output=True, text=True, timeout=60)
+        hipcc_version = [ln for ln in r.stdout.splitlines() if ln.strip()][:2]
+    except Exception:
+        hipcc_version = None
+    h = hashlib.sha256()
+    with open(LIB_PATH, "rb") as f:
+        h.update(f.read())
+    return {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm_version,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "hipcc": hipcc_version,
+            "build_flags": [f.replace(ROOT, "<repo>") for f in B.device_flags()],
+            "per_file_flags": B.FILE_FLAGS, "libattn_sha256_16": h.hexdigest()[:16],
+            "cpu_model": cpu_model(), "host_affinity_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads()}
 
 
 def quantiles(xs):
@@ -329,6 +450,10 @@ def bench_fwd_bwd(args, hev, stream):
         "first_call": first,
         "dominant": dom,
         "dominant_timed": dom_stats,
+        "_probe": {k: outs[0][k].cpu() for k in ("o", "lse", "dq", "dk", "dv")},
+        "seeds": {"Q,K,V,dO of input sets 0,1,2": [[b + j for j in range(4)] for b in
+                                                     (w.seed_base, w.seed_base + 100,
+                                                      w.seed_base + 200)]},
     }
 
 
@@ -361,7 +486,10 @@ def bench_decode(args, hev, stream, reps):
     q = quantiles(per_call)
     kv = 2.0 * w.B * w.Hkv * w.Skv * w.d * 2
     algo = kv + 2.0 * w.B * w.Hq * w.d * 2 + w.B * w.Hq * 4
-    return {"workload": "gqa_decode: bf16, B8 Hq32 Hkv8 Skv4096 d128, 16 splits",
+    torch.cuda.synchronize()
+    probe = (w, make_workload(w, w.seed_base), outs[0][0].cpu(), outs[0][1].cpu())
+    return {"_probe": probe, "seeds": [w.seed_base + 100 * i for i in range(3)],
+            "workload": "gqa_decode: bf16, B8 Hq32 Hkv8 Skv4096 d128, 16 splits",
             "us_median": q["median"] * 1e3, "us_p10": q["p10"] * 1e3, "us_p90": q["p90"] * 1e3,
             "us_per_call_issued_back_to_back": total_ms / reps * 1e3,
             "GB/s": algo / (q["median"] * 1e-3) / 1e9,
@@ -398,7 +526,11 @@ def bench_decode_paged(args, hev, stream, reps):
     keys = sum(w["lens"])
     algo = (2.0 * keys * w["Hkv"] * w["d"] * 2 + 2.0 * w["B"] * w["Hq"] * w["d"] * 2
             + w["B"] * w["Hq"] * 4 + w["B"] * (w["max_pages"] + 1) * 4)
-    return {"workload": "paged_decode: bf16, B8 Hq32 Hkv8 d128, 4096 keys per stream in "
+    torch.cuda.synchronize()
+    probe = (make_paged(w["B"], w["Hq"], w["Hkv"], w["d"], w["page_size"], w["max_pages"],
+                        w["lens"], seed=w["seed"]), scale, outs[0][0].cpu(), outs[0][1].cpu())
+    return {"_probe": probe, "seeds": [w["seed"] + 100 * i for i in range(3)],
+            "workload": "paged_decode: bf16, B8 Hq32 Hkv8 d128, 4096 keys per stream in "
                         "shuffled 64-key pages, 16 splits",
             "us_median": q["median"] * 1e3, "us_p10": q["p10"] * 1e3, "us_p90": q["p90"] * 1e3,
             "us_per_call_issued_back_to_back": total_ms / reps * 1e3,
@@ -616,7 +748,9 @@ def bench_small(args, hev, stream, reps):
                   + w.B * w.Hq * w.Sq * 4)
         peak_f = (157.3 if w.dtype == "f32" else PEAK_BF16_TFLOPS) * 1e12
         floor_us = max(flop / peak_f, nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
-        r = {"workload": f"{key}: {w.title}", "dtype": w.dtype,
+        torch.cuda.synchronize()
+        r = {"_probe": (w, make_workload(w), o.cpu(), lse.cpu()), "seed": w.seed_base,
+             "workload": f"{key}: {w.title}", "dtype": w.dtype,
              "us_median": res["cold"]["median"] * 1e3, "us_p10": res["cold"]["p10"] * 1e3,
              "us_p90": res["cold"]["p90"] * 1e3, "us_median_warm": res["warm"]["median"] * 1e3,
              "FLOP": flop, "algorithmic_bytes": nbytes,
@@ -650,7 +784,12 @@ def bench_prefill(args, hev, stream, reps):
     ms = [t[0] for t in times["fwd"] if t[0] is not None]
     q = quantiles(ms)
     fl = flops_fwd(w)
-    return {"workload": "long_prefill: bf16 causal, B1 Hq16 Hkv2 S44032 d256",
+    torch.cuda.synchronize()
+    rows = list(range(8)) + list(range(w.Sq - 8, w.Sq))
+    idx = torch.tensor(rows, device="cuda")
+    probe = (w, make_workload(w), rows, o[:, :, idx].cpu(), lse[:, :, idx].cpu())
+    return {"_probe": probe, "seed": w.seed_base,
+            "workload": "long_prefill: bf16 causal, B1 Hq16 Hkv2 S44032 d256",
             "ms_median": q["median"], "ms_p10": q["p10"], "ms_p90": q["p90"],
             "TFLOP/s": fl / (q["median"] * 1e-3) / 1e12,
             "frac_of_bf16_peak": fl / (q["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
@@ -681,17 +820,22 @@ def main():
     hev = HipEvents()
     stream = torch.cuda.current_stream()
 
+    def strip(d):
+        if isinstance(d, dict):
+            return {k: strip(v) for k, v in d.items() if k != "_probe"}
+        return d
+
     if args.only == "decode":
-        print(json.dumps(bench_decode(args, hev, stream, args.steps)), flush=True)
+        print(json.dumps(strip(bench_decode(args, hev, stream, args.steps))), flush=True)
         return
     if args.only == "paged_decode":
-        print(json.dumps(bench_decode_paged(args, hev, stream, args.steps)), flush=True)
+        print(json.dumps(strip(bench_decode_paged(args, hev, stream, args.steps))), flush=True)
         return
     if args.only == "small":
-        print(json.dumps(bench_small(args, hev, stream, args.steps)), flush=True)
+        print(json.dumps(strip(bench_small(args, hev, stream, args.steps))), flush=True)
         return
     if args.only == "prefill":
-        print(json.dumps(bench_prefill(args, hev, stream, args.steps)), flush=True)
+        print(json.dumps(strip(bench_prefill(args, hev, stream, args.steps))), flush=True)
         return
 
     w, cpu0, r = bench_fwd_bwd(args, hev, stream)
@@ -731,11 +875,21 @@ def main():
                 "peak": PEAK_BF16_TFLOPS if d["bound"] == "mfma" else PEAK_HBM_GBS,
                 "unit": d["unit"], "frac": d["frac"], "traffic": traffic,
                 "avg_us": d["avg_us"], "work_per_launch": d["work_per_launch"]}
+    probes = {}
+    for key in ("decode", "paged_decode", "long_prefill"):
+        if key in extras:
+            probes[key] = extras[key].pop("_probe")
+    if "small_fwd" in extras:
+        for key, r_small in extras["small_fwd"].items():
+            probes[key] = r_small.pop("_probe")
+    gpu_out = r.pop("_probe")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, cpu0)
+        cpu = cpu_baseline(w, cpu0, gpu_out)
         print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads",
               file=sys.stderr, flush=True)
+        if probes:
+            cpu["parity_other_workloads"] = parity_extras(extras, probes)
     line = {
         "metric": METRIC,
         "value": r["value"],
@@ -760,6 +914,8 @@ def main():
         "bwd": r["bwd"],
         "kernels": ks,
         "first_call": r["first_call"],
+        "seeds": r["seeds"],
+        "run_conditions": run_conditions(),
     }
     line.update(extras)
     if not args.no_extras and args.only is None:

@@ -137,9 +137,15 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int n_splits);
  * computes each split's unnormalised state (m, l, acc) for all Hq / Hkv
  * query heads of a key/value head in one pass over that split's keys and
  * values; a second kernel folds the n_splits states of each query with the
- * monoid merge and writes O = acc / l and lse = m + ln l.  The merge is
- * associative and commutative, so every partition gives the same result up
- * to rounding.  1 <= n_splits <= 256, else ATTN_ERR_VALUE.
+ * monoid merge and writes O = acc / l and lse = m + ln l.  The state
+ * (m, l, acc) is the one the blockwise recurrence of "Compilers and
+ * Kernels" (section "FlashAttention changes the algorithm around IO", second
+ * display equation) carries, and the merge is the monoid operation that
+ * "Tang, a compiler that derives GPU kernels and bounds how fast they can
+ * run" (Abstract) recognises online softmax as: both states rescaled to the
+ * larger maximum and added.  It is associative and commutative, so every
+ * partition gives the same result up to rounding.  1 <= n_splits <= 256,
+ * else ATTN_ERR_VALUE.
  * Supported d: {64, 128, 256} for both dtypes.
  */
 attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
