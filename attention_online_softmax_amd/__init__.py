@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     attn_bwd_fused_workspace_bytes,
     attn_bwd_workspace_bytes,
     attn_decode,
+    attn_decode_noalloc,
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,

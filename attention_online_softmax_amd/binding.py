@@ -25,7 +25,8 @@ STATUS_NAMES = {
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
            "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_fused_workspace_bytes",
-           "attn_bwd_fused", "attn_set_timing_events")
+           "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc")
+SCRATCH_BYTES = 8 << 20   # ATTN_SCRATCH_BYTES of attn.h
 
 _lib = None
 
@@ -59,6 +60,8 @@ def lib():
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode.restype = i
     L.attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode_noalloc.restype = i
+    L.attn_decode_noalloc.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_decode_paged.restype = i
     L.attn_decode_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp,
                                     sz, vp]
@@ -204,6 +207,31 @@ def attn_decode(q, k_cache, v_cache, scale=None, n_splits=16, o=None, lse=None,
                            _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_decode")
+    return o, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, scale=None, n_splits=16, o=None, lse=None,
+                        stream=None):
+    """attn_decode with the split states in the library's static device
+    scratch instead of a workspace (the library allocates nothing; outputs
+    are allocated here only if not passed).  Calls that overlap on one GPU
+    race on that scratch.  Returns (o, lse)."""
+    _check([q, k_cache, v_cache], ["q", "k_cache", "v_cache"])
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per head: q must be [B, Hq, 1, d]")
+    Hkv, Skv = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, 1), device=q.device, dtype=torch.float32)
+    st = lib().attn_decode_noalloc(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                   _ptr(lse), B, Hq, Hkv, Skv, d, float(scale), int(n_splits),
+                                   _stream(stream, q.device))
+    if st:
+        raise AttnError(st, "attn_decode_noalloc")
     return o, lse
 
 

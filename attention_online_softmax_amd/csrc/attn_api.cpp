@@ -9,6 +9,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -96,7 +98,9 @@ const char* attn_status_str(int s) {
     case ATTN_ERR_UNSUPPORTED: return "head dim or dtype not compiled for this entry point";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
-    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace missing or too small (attn_decode_noalloc: the split states need more "
+             "than the library's static scratch of ATTN_SCRATCH_BYTES bytes)";
     case ATTN_ERR_HIP: return "HIP launch failed";
     case ATTN_ERR_VALUE: return "invalid scalar argument (scale not finite or n_splits out of range)";
   }
@@ -157,9 +161,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int n_splits) {
   return round256((size_t)n_splits * B * Hq * (size_t)(d + 2) * sizeof(float));
 }
 
-attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
-                        float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
-                        int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by attn_decode and attn_decode_noalloc (which has
+// no caller workspace: check_ws false leaves the workspace out).
+attn_status check_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                         void* o, float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                         int n_splits, void* workspace, size_t workspace_bytes,
+                         bool check_ws = true) {
   if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -167,10 +178,14 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
   if (!decode_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   if (n_splits < 1 || n_splits > kMaxSplits) return ATTN_ERR_VALUE;
-  if (!workspace) return ATTN_ERR_WORKSPACE;
-  if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, d, n_splits)) return ATTN_ERR_WORKSPACE;
+  if (check_ws) {
+    if (!workspace) return ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, d, n_splits))
+      return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  }
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-      (lse && !aligned16(lse)) || !aligned16(workspace))
+      (lse && !aligned16(lse)))
     return ATTN_ERR_ALIGN;
   const int es = esize(dtype);
   const Span ins[3] = {span(q, (int64_t)B * Hq * d * es),
@@ -178,8 +193,21 @@ attn_status attn_decode(int dtype, const void* q, const void* k_cache, const voi
                        span(v_cache, (int64_t)B * Hkv * Skv * d * es)};
   const Span outs[3] = {span(o, (int64_t)B * Hq * d * es),
                         lse ? span(lse, (int64_t)B * Hq * 4) : Span{0, 0},
-                        span(workspace, (int64_t)attn_decode_workspace_bytes(B, Hq, d, n_splits))};
-  attn_status st = check_alias(outs, 3, ins, 3);
+                        check_ws ? span(workspace, (int64_t)attn_decode_workspace_bytes(
+                                                       B, Hq, d, n_splits))
+                                 : Span{0, 0}};
+  return check_alias(outs, 3, ins, 3);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
+                        float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                        int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  const attn_status st = check_decode(dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d,
+                                      scale, n_splits, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   attn::DecodeArgs a{dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, n_splits, scale,
                      (float*)workspace, (hipStream_t)stream};
@@ -222,6 +250,61 @@ attn_status attn_decode_paged(int dtype, const void* q, const void* k_pages, con
   attn::DecodeArgs a{dtype, q, k_pages, v_pages, o, lse, B, Hq, Hkv, 0, d, n_splits, scale,
                      (float*)workspace, (hipStream_t)stream,
                      attn::PagedKV{block_table, seq_lens, max_pages, page_size, n_pages}};
+  return hip_status(attn::launch_decode(a));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Static scratch for attn_decode_noalloc: the split states live in this
+// array instead of a caller's workspace.  Every device the library runs on
+// holds its own copy for the life of the process.  On the host, `scratch`
+// only names the symbol; its device address (one per device) comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[ATTN_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device), or an error.
+attn_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_noalloc(int dtype, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse, int B, int Hq, int Hkv,
+                                int Skv, int d, float scale, int n_splits, void* stream) {
+  // A problem whose split states exceed the static array is rejected before
+  // anything is enqueued.
+  if (attn_decode_workspace_bytes(B, Hq, d, n_splits) > ATTN_SCRATCH_BYTES)
+    return ATTN_ERR_WORKSPACE;
+  attn_status st = check_decode(dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, scale,
+                                n_splits, nullptr, 0, false);
+  if (st != ATTN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != ATTN_OK) return st;
+  attn::DecodeArgs a{dtype, q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, n_splits, scale,
+                     (float*)ws, (hipStream_t)stream};
   return hip_status(attn::launch_decode(a));
 }
 

@@ -18,7 +18,8 @@
  *   (memory from hipMalloc or a framework allocator on the current device).
  *   The caller owns every buffer, including workspaces; the library never
  *   allocates or frees device memory, keeps no state between calls and does
- *   not synchronise.
+ *   not synchronise.  (One exception: attn_decode_noalloc keeps its split
+ *   states in a static device array of the library, see there.)
  * Layout.  Dense, contiguous [B, H, S, d] (d innermost) for Q, K, V, O, dO,
  *   dQ, dK, dV; [B, Hq, Sq] float32 for LSE.  K and V share Hkv heads; query
  *   head h reads key/value head h / (Hq / Hkv) (grouped-query attention).
@@ -187,6 +188,34 @@ attn_status attn_decode_paged(int dtype, const void* q, const void* k_pages, con
                               int B, int Hq, int Hkv, int d, int n_pages, int page_size,
                               int max_pages, float scale, int n_splits, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* Bytes of the static device scratch that attn_decode_noalloc uses in place
+ * of a workspace (8 MiB per device, held until the process ends). */
+#define ATTN_SCRATCH_BYTES (8u << 20)
+
+/*
+ * attn_decode without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels, with the split states kept in a
+ * static device array of ATTN_SCRATCH_BYTES bytes inside the library (one
+ * per device, reserved for the life of the process) instead of a caller's
+ * workspace.  The call allocates and frees nothing.
+ *   Arguments, layouts, results and errors as attn_decode, without
+ *   workspace and workspace_bytes; a problem whose states need more than
+ *   ATTN_SCRATCH_BYTES, i.e. attn_decode_workspace_bytes(B, Hq, d, n_splits)
+ *   > ATTN_SCRATCH_BYTES, returns ATTN_ERR_WORKSPACE with nothing launched.
+ *   The first call on a device looks up that device's copy of the array
+ *   (ATTN_ERR_HIP if that fails).
+ * Every call on one device uses that device's one array: calls that overlap
+ * on a device (other streams, other host threads) race on it and give
+ * undefined results; serialise them.  Nothing in the array has to start at
+ * any value (every split state is written before it is read), and it keeps
+ * the last call's states.
+ */
+attn_status attn_decode_noalloc(int dtype, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Skv, int d, float scale,
+                                int n_splits, void* stream);
 
 /* Workspace for attn_bwd: 2 * B * Hq * Sqp float32 values, Sqp = Sq rounded
  * up to a multiple of 32 (per query row D_i = dO_i . O_i and

@@ -148,6 +148,33 @@ def test_decode_validation():
     assert call(scale=float("-inf")) == VALUE
 
 
+def test_decode_noalloc_validation():
+    """attn_decode_noalloc rejects bad arguments, and problems whose split
+    states exceed the static scratch, before touching the device."""
+    f = Fake()
+    q, k, v, o, lse = (f() for _ in range(5))
+    L = aos.lib()
+
+    def call(**kw):
+        a = dict(dt=BF16, q=q, k=k, v=v, o=o, lse=lse, B=2, Hq=8, Hkv=2, Skv=4096, d=128,
+                 scale=0.1, n=16)
+        a.update(kw)
+        return L.attn_decode_noalloc(a["dt"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                     a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"], a["n"], None)
+
+    assert call(k=None) == NULL
+    assert call(Hq=6, Hkv=4) == SHAPE
+    assert call(d=80) == UNSUP
+    assert call(n=0) == VALUE
+    assert call(scale=float("nan")) == VALUE
+    assert call(o=q) == ALIAS
+    assert call(q=q + 8) == ALIGN
+    # 256 splits x 64 x 64 heads x 130 floats: 545 MB of split states
+    assert aos.attn_decode_workspace_bytes(64, 64, 128, 256) > aos.binding.SCRATCH_BYTES
+    assert call(B=64, Hq=64, Hkv=8, n=256) == WS
+    assert "static scratch" in aos.attn_status_str(WS)
+
+
 def test_decode_paged_validation():
     f = Fake()
     q, kp, vp, tab, lens, o, lse, ws = (f() for _ in range(8))
