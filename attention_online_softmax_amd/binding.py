@@ -25,7 +25,8 @@ STATUS_NAMES = {
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
            "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_fused_workspace_bytes",
-           "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc")
+           "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc",
+           "attn_fwd_tile_plan", "attn_fwd_tile_override")
 SCRATCH_BYTES = 8 << 20   # ATTN_SCRATCH_BYTES of attn.h
 
 _lib = None
@@ -75,6 +76,11 @@ def lib():
     L.attn_bwd_fused.restype = i
     L.attn_bwd_fused.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  i, i, i, i, i, i, i, f, vp, sz, vp]
+    ip, fp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)
+    L.attn_fwd_tile_plan.restype = i
+    L.attn_fwd_tile_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, fp, ip]
+    L.attn_fwd_tile_override.restype = i
+    L.attn_fwd_tile_override.argtypes = [i, i]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -104,6 +110,27 @@ def attn_set_timing_events(events):
         st = lib().attn_set_timing_events(arr, len(events))
     if st:
         raise AttnError(st, "attn_set_timing_events")
+
+
+def attn_fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv):
+    """The bf16 forward's tile candidates for a shape: a list of
+    {"nw", "bc", "est_us"} and the index the estimate picks (None, [] for an
+    unsupported head dim or shape)."""
+    cap = 16
+    nw, bc = (ctypes.c_int * cap)(), (ctypes.c_int * cap)()
+    est, pick = (ctypes.c_float * cap)(), ctypes.c_int(-1)
+    n = lib().attn_fwd_tile_plan(int(d), int(bool(causal)), B, Hq, Hkv, Sq, Skv, cap, nw, bc, est,
+                                 ctypes.byref(pick))
+    cands = [{"nw": nw[i], "bc": bc[i], "est_us": est[i]} for i in range(min(n, cap))]
+    return (pick.value if n else None), cands
+
+
+def attn_fwd_tile_override(nw=0, bc=0):
+    """Force (waves per workgroup, keys per tile) on this thread's later bf16
+    forward calls without window or bias; (0, 0) returns to the estimate."""
+    st = lib().attn_fwd_tile_override(int(nw), int(bc))
+    if st:
+        raise AttnError(st, "attn_fwd_tile_override")
 
 
 def attn_decode_workspace_bytes(B, Hq, d, n_splits):

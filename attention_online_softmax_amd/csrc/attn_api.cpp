@@ -107,6 +107,20 @@ const char* attn_status_str(int s) {
   return "unknown status";
 }
 
+attn_status attn_fwd_tile_override(int nw, int bc) {
+  if ((nw == 0) != (bc == 0) || nw < 0 || bc < 0) return ATTN_ERR_VALUE;
+  attn::fwd_tile_set_override(nw, bc);
+  return ATTN_OK;
+}
+
+int attn_fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap,
+                       int* nw, int* bc, float* est_us, int* pick) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || cap < 0)
+    return 0;
+  if (causal && Sq > Skv) return 0;
+  return attn::fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv, cap, nw, bc, est_us, pick);
+}
+
 attn_status attn_set_timing_events(void* const* events, int n) {
   if (n < 0) return ATTN_ERR_VALUE;
   g_events = (events && n > 0) ? events : nullptr;
@@ -138,6 +152,8 @@ attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
   if (!fwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   // bf16 with a bias: d <= 128 (the d256 kernel has no registers to spare).
   if (bias && dtype == ATTN_BF16 && d > 128) return ATTN_ERR_UNSUPPORTED;
+  // A forced tile shape (attn_fwd_tile_override) must be compiled for d.
+  if (dtype == ATTN_BF16 && !attn::fwd_tile_override_ok(d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   int64_t bias_bytes = 0;
   attn_status st = check_bias(bias, bias_sb, bias_sh, B, Hq, Sq, Skv, &bias_bytes);

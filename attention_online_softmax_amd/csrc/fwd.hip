@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 // bf16 path: 32x32x16 bf16 MFMA with fp32 accumulation.
 //
-// Four (d64, d128) or eight (d256) waves per workgroup, 32 query rows per
+// NW (2, 4 or 8, chosen per call) waves per workgroup, 32 query rows per
 // wave; the waves share every K/V tile.  Scores are formed
 // transposed, S^T = K Q^T (A = key rows from LDS, B = the wave's queries held
 // in registers), so each lane owns ONE query column and 16 of its scores per
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
 // V tile through LDS transpose reads.  The accumulator O^T is again indexed
 // by the lane's query, so rescaling by alpha is a per-lane scalar.
 //
-// K/V tiles of BC keys (32; 64 at d64, see kFwdKeys) go from HBM straight
+// K/V tiles of BC keys (32 or 64, chosen per call) go from HBM straight
 // into LDS with buffer loads to LDS (no staging registers), double-buffered:
 // tile j+1 is requested when tile j's loop body starts.  Tiles are dense
 // [BC][D] with 16-byte chunks XOR-swizzled per row (tile_swz) so that the K
@@ -234,22 +234,23 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
 constexpr float kLazy = 8.f;
 constexpr float kLazyBound = 256.f;   // 2^kLazy
 
-// Keys per K/V tile.  d64 takes 64-key tiles: a 32-key tile gives each wave
-// only 8 products between barriers, and the wider tile (32 KB of LDS per
-// workgroup, as d128 with 32 keys) is 4-8 % faster on MI355X; d128 and d256
-// are fastest with 32 (the 64-key d128 tile costs a third workgroup per CU).
-// The bias path adds its values tile by tile for 32 keys.
-template <int D, bool BIAS>
-constexpr int kFwdKeys = (D == 64 && !BIAS) ? 64 : 32;
+// Keys per K/V tile (BC, 32 or 64) and waves per workgroup (NW, 32 query
+// rows each) are template parameters; the launcher picks them per call from
+// a per-tile time estimate (fwd_tiles.cpp).  The bias path adds its values
+// tile by tile for 32 keys.  Two waves per SIMD must fit (at most 256
+// registers), except for the eight-wave d256 kernel, which is the only
+// workgroup on its compute unit.
+template <int D, int NW>
+constexpr int kFwdMinWaves = (NW == 8 && D >= 256) ? 1 : 2;
 
-template <int D, bool CAUSAL, int NW, bool WIN, bool BIAS>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS>
+__global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW>)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
     int n_qtiles) {
+  static_assert(!BIAS || BC == 32, "the bias path works on 32-key tiles");
   constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
-  constexpr int BC = kFwdKeys<D, BIAS>;   // keys per tile
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
@@ -544,18 +545,9 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   return launch_fwd_f32_c<D, CAUSAL, D / 32, 256, 1>(a);
 }
 
-// Waves per workgroup: every wave holds 32 query rows, and all waves of a
-// workgroup share each K/V tile, so more waves cut the LDS fills (L2 reads)
-// per FLOP; d256 uses 8 (its 250 registers allow two waves per SIMD, one
-// such workgroup per CU), d64/d128 use 4 (two or three workgroups per CU).
-template <int D>
-constexpr int kFwdWaves = D >= 256 ? 8 : 4;
-
-// The sliding window is a template parameter: calls without one run the
-// kernel with none of its index arithmetic.
-template <int D, bool CAUSAL, bool WIN, bool BIAS>
-static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
-  constexpr int NW = kFwdWaves<D>;
+// One bf16 forward launch with NW waves per workgroup and BC keys per tile.
+template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS>
+static hipError_t launch_fwd_bf16_k(const FwdArgs& a) {
   const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
@@ -563,12 +555,78 @@ static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
   // workgroup per query head of each (see the kernel's work mapping).
   const int items = n_qtiles * a.B * a.Hkv;
   const int grid = (items + 7) / 8 * 8 * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, WIN, BIAS>), dim3(grid),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, WIN, BIAS>), dim3(grid),
                      dim3(64 * NW), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
                      a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
+}
+
+// Candidate (NW, BC) of the plain (no window, no bias) kernel: launch it, or
+// with fn != nullptr only report its function (for occupancy queries).
+template <int D, bool CAUSAL, int NW, int BC>
+static hipError_t fwd_candidate(const FwdArgs* a, const void** fn) {
+  if (fn) {
+    *fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, NW, BC, false, false>);
+    return hipSuccess;
+  }
+  return launch_fwd_bf16_k<D, CAUSAL, NW, BC, false, false>(*a);
+}
+
+template <int D, bool CAUSAL>
+static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
+  // Must list the candidates of fwd_tile_candidates() in the same order.
+  if constexpr (D == 64) {
+    switch (idx) {
+      case 0: return fwd_candidate<D, CAUSAL, 4, 64>(a, fn);
+      case 1: return fwd_candidate<D, CAUSAL, 4, 32>(a, fn);
+      case 2: return fwd_candidate<D, CAUSAL, 8, 64>(a, fn);
+      case 3: return fwd_candidate<D, CAUSAL, 2, 64>(a, fn);
+    }
+  } else if constexpr (D == 128) {
+    switch (idx) {
+      case 0: return fwd_candidate<D, CAUSAL, 4, 32>(a, fn);
+      case 1: return fwd_candidate<D, CAUSAL, 4, 64>(a, fn);
+      case 2: return fwd_candidate<D, CAUSAL, 8, 32>(a, fn);
+      case 3: return fwd_candidate<D, CAUSAL, 8, 64>(a, fn);
+    }
+  } else {
+    switch (idx) {
+      case 0: return fwd_candidate<D, CAUSAL, 8, 32>(a, fn);
+      case 1: return fwd_candidate<D, CAUSAL, 4, 32>(a, fn);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// Function of candidate idx of the plain bf16 forward (d, causal).
+hipError_t fwd_candidate_fn(int d, bool causal, int idx, const void** fn) {
+  switch (d) {
+    case 64: return causal ? fwd_candidate_i<64, true>(idx, nullptr, fn)
+                           : fwd_candidate_i<64, false>(idx, nullptr, fn);
+    case 128: return causal ? fwd_candidate_i<128, true>(idx, nullptr, fn)
+                            : fwd_candidate_i<128, false>(idx, nullptr, fn);
+    case 256: return causal ? fwd_candidate_i<256, true>(idx, nullptr, fn)
+                            : fwd_candidate_i<256, false>(idx, nullptr, fn);
+  }
+  return hipErrorInvalidValue;
+}
+
+// The sliding window and the additive bias are template parameters: calls
+// without them run the kernel with none of their arithmetic.  Plain calls
+// take the candidate the tile estimate picks; windowed or biased calls a
+// fixed shape (the bias path: 32-key tiles).
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
+static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
+  if constexpr (!WIN && !BIAS) {
+    const int idx = fwd_pick_candidate(a);
+    return fwd_candidate_i<D, CAUSAL>(idx, &a, nullptr);
+  } else {
+    constexpr int NW = D >= 256 ? 8 : 4;
+    constexpr int BC = (D == 64 && !BIAS) ? 64 : 32;
+    return launch_fwd_bf16_k<D, CAUSAL, NW, BC, WIN, BIAS>(a);
+  }
 }
 
 // An additive bias is a template parameter too (d <= 128: the d256 kernel

@@ -81,6 +81,14 @@ inline int device_cus() {
 void timing_mark(hipStream_t stream, int slot);
 
 hipError_t launch_fwd(const FwdArgs& a);
+// bf16 forward tile selection (fwd_tiles.cpp): index of the compiled
+// candidate (waves per workgroup, keys per tile) for a plain call; the
+// per-candidate estimates; a per-thread override for sweeps and tests.
+int fwd_pick_candidate(const FwdArgs& a);
+int fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap, int* nw,
+                  int* bc, float* est_us, int* pick);
+bool fwd_tile_override_ok(int d);
+void fwd_tile_set_override(int nw, int bc);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 // Fused variant (no window or bias): ws holds the (D, nl) pairs, then from

@@ -766,6 +766,87 @@ def bench_small(args, hev, stream, reps):
     return out
 
 
+# Shapes of the tile-selection leg: (B, Hq, Hkv, S, d, causal).  The
+# estimate's constants were calibrated on the first set; the second set was
+# not used for that and validates the picks.
+TILE_SHAPES_CAL = [
+    (4, 16, 16, 2048, 128, True),    # the training forward
+    (4, 16, 16, 512, 64, True),      # the transformer-block forward
+    (1, 16, 2, 44032, 256, True),    # the 44k-token prefill
+    (4, 16, 16, 1024, 64, True),
+    (4, 16, 16, 512, 128, True),
+    (1, 16, 16, 8192, 128, True),
+    (8, 16, 16, 1024, 128, False),
+    (4, 32, 4, 4096, 128, True),
+    (2, 16, 16, 4096, 64, False),
+    (16, 16, 16, 2048, 128, True),
+    (2, 16, 2, 16384, 256, True),
+    (1, 8, 8, 256, 128, False),
+]
+TILE_SHAPES_VAL = [
+    (2, 32, 8, 3072, 128, True),
+    (1, 32, 32, 4096, 64, True),
+    (8, 8, 8, 768, 128, True),
+    (4, 16, 4, 1536, 128, False),
+    (1, 16, 2, 8192, 256, True),
+    (2, 24, 24, 2048, 64, True),
+    (16, 16, 16, 512, 128, True),
+    (1, 64, 8, 6144, 128, True),
+]
+
+
+def bench_tile_selection(args, hev, stream, reps=10):
+    """Every compiled (waves per workgroup, keys per tile) candidate of the
+    bf16 forward timed on each shape (warm, median of `reps` calls, events
+    around the kernel), next to the per-tile estimate and the candidate it
+    picks ("Tang", Abstract: the estimate picks the tile)."""
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import make_qkv
+    rows = []
+    for (B, Hq, Hkv, S, d, causal), role in ([(x, "calibration") for x in TILE_SHAPES_CAL]
+                                            + [(x, "validation") for x in TILE_SHAPES_VAL]):
+        x = {k: v.cuda() for k, v in make_qkv(B, Hq, Hkv, S, S, d, seed=777).items()}
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+        pick, cands = aos.attn_fwd_tile_plan(d, causal, B, Hq, Hkv, S, S)
+        n_reps = reps if S < 16384 else max(3, reps // 3)
+        for c in cands:
+            aos.attn_fwd_tile_override(c["nw"], c["bc"])
+
+            def fwd(i):
+                aos.attn_fwd(x["q"], x["k"], x["v"], causal=causal, scale=d ** -0.5, o=o, lse=lse)
+
+            try:
+                fwd(0)
+                fwd(0)
+                torch.cuda.synchronize()
+                _, times, _ = run_calls([("fwd", fwd)], {"fwd": 1}, hev, n_reps, stream)
+            finally:
+                aos.attn_fwd_tile_override(0, 0)
+            c["measured_us"] = quantiles([t[0] for t in times["fwd"] if t[0] is not None])[
+                "median"] * 1e3
+        fastest = min(range(len(cands)), key=lambda i: cands[i]["measured_us"])
+        rows.append({"shape": f"B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} {'causal' if causal else 'full'}",
+                     "role": role,
+                     "candidates": cands, "pick": [cands[pick]["nw"], cands[pick]["bc"]],
+                     "fastest": [cands[fastest]["nw"], cands[fastest]["bc"]],
+                     "pick_over_fastest": cands[pick]["measured_us"] / cands[fastest]["measured_us"]})
+        print(f"[bench] tiles {rows[-1]['shape']}: pick {rows[-1]['pick']} "
+              f"{rows[-1]['pick_over_fastest']:.3f}x fastest {rows[-1]['fastest']}",
+              file=sys.stderr, flush=True)
+    out = {"shapes": rows}
+    for role in ("calibration", "validation"):
+        rr = [r for r in rows if r["role"] == role]
+        out[role] = {"picks_within_3pct": sum(r["pick_over_fastest"] <= 1.03 for r in rr),
+                     "n_shapes": len(rr),
+                     "worst_pick_over_fastest": max(r["pick_over_fastest"] for r in rr),
+                     "mean_pick_over_fastest": sum(r["pick_over_fastest"] for r in rr) / len(rr)}
+    out["picks_within_3pct"] = sum(r["pick_over_fastest"] <= 1.03 for r in rows)
+    out["n_shapes"] = len(rows)
+    return out
+
+
 def bench_prefill(args, hev, stream, reps):
     import torch
     import attention_online_softmax_amd as aos
@@ -802,8 +883,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill", "small"],
-                    default=None)
+    ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill", "small",
+                                       "tiles"], default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -837,6 +918,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps(strip(bench_prefill(args, hev, stream, args.steps))), flush=True)
         return
+    if args.only == "tiles":
+        print(json.dumps(bench_tile_selection(args, hev, stream)), flush=True)
+        return
 
     w, cpu0, r = bench_fwd_bwd(args, hev, stream)
     print(f"[bench] fwd+bwd: {r['ms_per_step']:.3f} ms/step, {r['value']:.1f} TFLOP/s",
@@ -862,6 +946,10 @@ def main():
         extras["small_fwd"] = bench_small(args, hev, stream, max(args.steps, 50))
         print(f"[bench] fp32 S128 fwd {extras['small_fwd']['fp32_small']['us_median']:.1f} us, "
               f"block fwd {extras['small_fwd']['block_fwd']['us_median']:.1f} us",
+              file=sys.stderr, flush=True)
+        extras["tile_selection"] = bench_tile_selection(args, hev, stream)
+        print(f"[bench] tile selection: {extras['tile_selection']['picks_within_3pct']} of "
+              f"{extras['tile_selection']['n_shapes']} picks within 3 % of the fastest",
               file=sys.stderr, flush=True)
         extras["long_prefill"] = bench_prefill(args, hev, stream, max(3, min(args.steps, 10)))
         print(f"[bench] long prefill: {extras['long_prefill']['ms_median']:.2f} ms",

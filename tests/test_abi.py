@@ -175,6 +175,20 @@ def test_decode_noalloc_validation():
     assert "static scratch" in aos.attn_status_str(WS)
 
 
+def test_fwd_tile_entry_points():
+    """Tile override: exactly one of (nw, bc) zero, or a negative value, is
+    rejected; plan: unsupported head dims and invalid shapes list nothing
+    (both checks happen before any device query)."""
+    L = aos.lib()
+    assert L.attn_fwd_tile_override(4, 0) == VALUE
+    assert L.attn_fwd_tile_override(0, 32) == VALUE
+    assert L.attn_fwd_tile_override(-4, -32) == VALUE
+    assert L.attn_fwd_tile_override(0, 0) == 0
+    assert aos.attn_fwd_tile_plan(80, True, 1, 1, 1, 64, 64) == (None, [])
+    assert aos.attn_fwd_tile_plan(128, True, 1, 3, 2, 64, 64) == (None, [])
+    assert aos.attn_fwd_tile_plan(128, True, 1, 2, 2, 65, 64) == (None, [])
+
+
 def test_decode_paged_validation():
     f = Fake()
     q, kp, vp, tab, lens, o, lse, ws = (f() for _ in range(8))
