@@ -20,7 +20,7 @@ namespace attn {
 // through K/V buffers of their own, and their states (m, l, o) are merged
 // by the monoid at the end.  That cuts the serial VALU work per row by 4.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int TPR, int NT, int KW>
+template <int D, bool CAUSAL, int TPR, int NT, int KW, bool BIAS>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
@@ -70,9 +70,9 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int kv_begin =
       (CAUSAL && window > 0) ? max(0, qtile * ROWS + off - window + 1) / BC * BC : 0;
-  // Additive bias row of this query (row i of the [Sq, Skv] bias plane).
-  const float* brow =
-      bias ? bias + b * bsb + h * bsh + (int64_t)min(row, Sq - 1) * Skv : nullptr;
+  // Additive bias row of this query (row i of the [Sq, Skv] bias plane); a
+  // template parameter, so calls without one carry no bias loads.
+  const float* brow = BIAS ? bias + b * bsb + h * bsh + (int64_t)min(row, Sq - 1) * Skv : nullptr;
 
   float m = kNegInf;
   KahanSum l{0.f, 0.f};
@@ -90,19 +90,21 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
       f32x4 kx[GRP], vx[GRP];
 #pragma unroll
       for (int i = 0; i < GRP; ++i) {
+        // Rows past the last key load the last row and are zeroed after
+        // (no branch around the loads).
         const int e = ((i0 + i) * NTR + ltid) * 4;
         const int key = k0 + e / D, c = e % D;
-        kx[i] = vx[i] = f32x4{0, 0, 0, 0};
-        if (key < Skv) {
-          kx[i] = *(const f32x4*)(Kh + (int64_t)key * D + c);
-          vx[i] = *(const f32x4*)(Vh + (int64_t)key * D + c);
-        }
+        const int64_t kr = (int64_t)min(key, Skv - 1) * D + c;
+        kx[i] = *(const f32x4*)(Kh + kr);
+        vx[i] = *(const f32x4*)(Vh + kr);
       }
 #pragma unroll
       for (int i = 0; i < GRP; ++i) {
         const int e = ((i0 + i) * NTR + ltid) * 4;
-        *(f32x4*)(tK + e) = kx[i];
-        *(f32x4*)(tV + e) = vx[i];
+        const bool in = k0 + e / D < Skv;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(tK + e) = in ? kx[i] : zero;
+        *(f32x4*)(tV + e) = in ? vx[i] : zero;
       }
     }
     if (KW == 1) __syncthreads();
@@ -121,11 +123,10 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
         acc = fmaf(q[c + 3], kx[3], acc);
       }
       acc = group_reduce<TPR, false>(acc);
-      float x = kNegInf;
-      if (k0 + j < row_limit && k0 + j >= row_lo)
-        x = brow ? fmaf(brow[k0 + j], kLog2e, acc * scale_log2) : acc * scale_log2;
-      s[j] = x;
-      mx = fmaxf(mx, x);
+      float x = acc * scale_log2;
+      if constexpr (BIAS) x = fmaf(brow[min(k0 + j, Skv - 1)], kLog2e, x);
+      s[j] = (k0 + j < row_limit && k0 + j >= row_lo) ? x : kNegInf;
+      mx = fmaxf(mx, s[j]);
     }
     const float msub = (mx == kNegInf) ? 0.f : mx;
     const float alpha = fast_exp2(m - msub);
@@ -520,19 +521,25 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW>)) void fwd_bf16_kerne
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int TPR, int NT, int KW>
-static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
+template <int D, bool CAUSAL, int TPR, int NT, int KW, bool BIAS>
+static hipError_t launch_fwd_f32_k(const FwdArgs& a) {
   constexpr int ROWS = NT / KW / TPR;
   const int n_qtiles = (a.Sq + ROWS - 1) / ROWS;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT, KW>), dim3(n_qtiles * BH), dim3(NT), 0,
-                     a.stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT, KW, BIAS>), dim3(n_qtiles * BH), dim3(NT),
+                     0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
                      a.scale * kLog2e, n_qtiles);
   timing_mark(a.stream, 1);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, int TPR, int NT, int KW>
+static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
+  if (a.bias) return launch_fwd_f32_k<D, CAUSAL, TPR, NT, KW, true>(a);
+  return launch_fwd_f32_k<D, CAUSAL, TPR, NT, KW, false>(a);
 }
 
 // Fewer 256-thread workgroups than compute units: 8 columns per lane and
