@@ -15,10 +15,11 @@ namespace attn {
 // Large grids use 256-thread workgroups with 32 columns per lane (KW = 1:
 // the four waves hold different rows and share every K/V tile).  Grids that
 // would not fill the compute units use 8 columns per lane, which spreads
-// the rows over 4 D/32 times as many workgroups, and KW = 4: the four waves
-// of a workgroup hold the same rows and take every fourth key tile each,
-// through K/V buffers of their own, and their states (m, l, o) are merged
-// by the monoid at the end.  That cuts the serial VALU work per row by 4.
+// the rows over 4 D/32 times as many workgroups, and KW = 8 (d <= 128, 16-key
+// tiles) or 4 (d = 256): the waves of a workgroup hold the same rows and
+// take every KW-th key tile each, through K/V buffers of their own, and
+// their states (m, l, o) are merged by the monoid at the end.  That cuts
+// the serial VALU work per row by KW.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int TPR, int NT, int KW, bool BIAS>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(
   constexpr int CPL = D / TPR;         // columns per lane
   constexpr int NTR = NT / KW;         // threads that share a K/V tile
   constexpr int ROWS = NTR / TPR;      // query rows per workgroup
-  constexpr int BC = (KW > 1 && D >= 256) ? 16 : 32;   // keys per LDS tile
+  constexpr int BC = (KW > 4 || (KW > 1 && D >= 256)) ? 16 : 32;   // keys per LDS tile
   __shared__ float sK[KW * BC * D];
   __shared__ float sV[KW * BC * D];
 
@@ -543,12 +544,19 @@ static hipError_t launch_fwd_f32_c(const FwdArgs& a) {
 }
 
 // Fewer 256-thread workgroups than compute units: 8 columns per lane and
-// the keys split over the four waves of each workgroup.
+// the keys split over the waves of each workgroup.
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
   constexpr int ROWS = 256 / (D / 32);
   const int64_t big = (int64_t)((a.Sq + ROWS - 1) / ROWS) * a.B * a.Hq;
-  if (big < device_cus()) return launch_fwd_f32_c<D, CAUSAL, D / 8, 256, 4>(a);
+  if (big < device_cus()) {
+    // d <= 128: eight waves of 16-key tiles (their K/V buffers fit in LDS);
+    // d = 256: four waves.
+    if constexpr (D <= 128)
+      return launch_fwd_f32_c<D, CAUSAL, D / 8, 512, 8>(a);
+    else
+      return launch_fwd_f32_c<D, CAUSAL, D / 8, 256, 4>(a);
+  }
   return launch_fwd_f32_c<D, CAUSAL, D / 32, 256, 1>(a);
 }
 
