@@ -115,13 +115,16 @@ def attn_set_timing_events(events):
 def attn_fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv):
     """The bf16 forward's tile candidates for a shape: a list of
     {"nw", "bc", "est_us"} and the index the estimate picks (None, [] for an
-    unsupported head dim or shape)."""
+    unsupported head dim or shape).  nw < 0 is the key-split kernel (|nw|
+    waves on one 32-row query block); est_us is None where a candidate does
+    not apply to the shape."""
     cap = 16
     nw, bc = (ctypes.c_int * cap)(), (ctypes.c_int * cap)()
     est, pick = (ctypes.c_float * cap)(), ctypes.c_int(-1)
     n = lib().attn_fwd_tile_plan(int(d), int(bool(causal)), B, Hq, Hkv, Sq, Skv, cap, nw, bc, est,
                                  ctypes.byref(pick))
-    cands = [{"nw": nw[i], "bc": bc[i], "est_us": est[i]} for i in range(min(n, cap))]
+    cands = [{"nw": nw[i], "bc": bc[i], "est_us": est[i] if math.isfinite(est[i]) else None}
+             for i in range(min(n, cap))]
     return (pick.value if n else None), cands
 
 

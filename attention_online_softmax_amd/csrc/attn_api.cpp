@@ -108,7 +108,7 @@ const char* attn_status_str(int s) {
 }
 
 attn_status attn_fwd_tile_override(int nw, int bc) {
-  if ((nw == 0) != (bc == 0) || nw < 0 || bc < 0) return ATTN_ERR_VALUE;
+  if ((nw == 0) != (bc == 0) || bc < 0) return ATTN_ERR_VALUE;
   attn::fwd_tile_set_override(nw, bc);
   return ATTN_OK;
 }

@@ -520,6 +520,250 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW>)) void fwd_bf16_kerne
 }
 
 // ---------------------------------------------------------------------------
+// bf16 key-split forward, for grids with few query blocks per compute unit.
+//
+// A workgroup of NW waves takes ONE 32-row query block, and its waves split
+// the block's 32-key tiles: wave w takes tiles w, w + NW, w + 2 NW, ...,
+// each wave with its own online-softmax state (m, l, o).  The NW states of
+// every row are then merged through LDS with the monoid operation ("Tang, a
+// compiler that derives GPU kernels and bounds how fast they can run",
+// Abstract: online softmax as a monoid; the same merge as the split-KV
+// decode).  A heavy causal query block then takes about
+// 1/NW of its key tiles in time instead of all of them.
+//
+// No tile is shared between waves, so there is no barrier in the loop.  Key
+// rows go from HBM straight into the MFMA A-operand registers (the wave's
+// next tile is requested when the current one starts); V tiles go through a
+// per-wave double buffer in LDS, for the transpose reads.  Scores, softmax
+// and P V are those of fwd_bf16_kernel for one wave and one 32-key block.
+// ---------------------------------------------------------------------------
+// One 32-key block of the online softmax with the lazy reference of
+// fwd_bf16_kernel: the block's exponentials against m_ref, packed as the B
+// operand of the P V product; the reference moves (and the returned factor
+// differs from 1) only when they would reach 2^kLazy.
+__device__ __forceinline__ float softmax_block(const f32x16& s, u32x4 (&pb)[2], float& m_ref,
+                                               KahanSum& lpart, float c2) {
+  auto exps = [&](float msub) __attribute__((always_inline)) {
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(fmaf(s[8 * c + 2 * j], c2, -msub));
+        const float p1 = fast_exp2(fmaf(s[8 * c + 2 * j + 1], c2, -msub));
+        sum += p0 + p1;
+        pb[c][j] = pack_bf16x2(p0, p1);
+      }
+    return sum;
+  };
+  float lsum = exps(m_ref);
+  float alpha = 1.f;
+  if (__any(!(lsum < kLazyBound))) {
+    float rmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[i]);
+    const float mnew = fmaxf(m_ref, halfwave_max(rmax) * c2);
+    alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m_ref - mnew);
+    m_ref = mnew;
+    lsum = exps((m_ref == kNegInf) ? 0.f : m_ref);
+  }
+  lpart.scale(alpha);
+  lpart.add(lsum);
+  return alpha;
+}
+
+// Taken only where the grid has at most one query block per compute unit,
+// so two waves per SIMD are plenty (no register cap below 256).
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_ks_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
+    float scale_log2, int n_qtiles) {
+  constexpr int BC = 32;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int VBUF = BC * D;   // one V tile, bf16 elements
+  // Per-wave V buffers, as two arrays (distinct objects: the compiler sees
+  // which buffer a transfer writes and a read reads).  After the loop they
+  // hold the waves' o rows for the merge: rows 0-15 of wave w in sV0's part
+  // of wave w, rows 16-31 in sV1's (16 rows x D floats = one V tile).
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[NW * VBUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[NW * VBUF];
+  __shared__ float sML[NW * 32 * 2];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 31, g = lane >> 5;
+  // Work item and XCD grouping as in fwd_bf16_kernel.
+  const int G = Hq / Hkv;
+  const int BHk = BH / G;
+  const int qq = blockIdx.x >> 3;
+  const int r = (qq / G) * 8 + (blockIdx.x & 7);
+  if (r >= n_qtiles * BHk) return;
+  const int t = r / BHk;
+  const int b = (r % BHk) / Hkv, hk = (r % BHk) % Hkv;
+  const int h = hk * G + qq % G;
+  const int bh = b * Hq + h;
+  const int qtile = CAUSAL ? (n_qtiles - 1 - t) : t;
+  const int off = Skv - Sq;
+  const int q0 = qtile * 32;
+  const int row = q0 + n;
+
+  const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
+  const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
+  const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
+  const int last_row = min(q0 + 32, Sq) - 1;
+  const int kv_end = CAUSAL ? max(0, min(Skv, last_row + off + 1)) : Skv;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  int t_mask = Skv / BC;   // tiles from t_mask on cut some row's key range
+  if (CAUSAL) t_mask = min(t_mask, (q0 + off + 1) / BC);
+
+  // Scale sign and zero scale as in fwd_bf16_kernel.
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const uint32_t qkeep = scale_log2 == 0.f ? 0u : 0xffffffffu;
+  const float c2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
+  u32x4 qreg[NDC];
+  const int qrow = min(row, Sq - 1);
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
+    qreg[c] = (qreg[c] ^ qsign) & qkeep;
+  }
+
+  // Key rows: lane (n, g) holds row swap23(n) of the tile, columns
+  // 8 (2c + g) .. +7 for k-step c, loaded through a buffer resource over the
+  // whole [Skv, D] matrix (rows past Skv read as zeros).
+  const rsrc_t rk = make_rsrc(Kh, (uint32_t)Skv * D * 2);
+  const int kvoff = (swap23(n) * D + 8 * g) * 2;
+  auto load_k = [&](int j, u32x4* kr) __attribute__((always_inline)) {
+    const int soff = (int)((uint32_t)j * BC * D * 2);
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) kr[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvoff + 32 * c, soff, 0);
+  };
+  TileDma<D, BC, 1> dma;
+  dma.init(0, lane);
+  uint16_t* v0 = sV0 + wave * VBUF;
+  uint16_t* v1 = sV1 + wave * VBUF;
+  int v_off[kTrOffs<D>];
+  tr_read_offsets<D>(lane, v_off);
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_ref = kNegInf;
+  KahanSum lpart{0.f, 0.f};
+  const int row_limit = CAUSAL ? min(row + off + 1, Skv) : Skv;
+
+  u32x4 kA[NDC], kB[NDC];
+  auto step = [&](int j, const u32x4* kc, u32x4* kn, const uint16_t* cV, uint16_t* nV)
+      __attribute__((always_inline)) {
+    wait_vmcnt0();   // tile j's key rows and V tile have landed
+    opaque_offsets<kTrOffs<D>>(v_off);
+    if (j + NW < n_tiles) {
+      load_k(j + NW, kn);
+      dma.load(Vh, Skv, nV, (j + NW) * BC, 0);
+    }
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) s = mfma32(kc[c], qreg[c], s);
+    if (j >= t_mask) {
+      const int lim = row_limit - j * BC - 8 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 16 * (i >> 3) + (i & 7);
+        s[i] = kk < lim ? s[i] : kNegInf;
+      }
+    }
+    u32x4 p[2];
+    const float alpha = softmax_block(s, p, m_ref, lpart, c2);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(tr_col8<D>(cV + 16 * c * D, v_off, db), p[c], oacc[db]);
+  };
+  if (wave < n_tiles) {
+    load_k(wave, kA);
+    dma.load(Vh, Skv, v0, wave * BC, 0);
+  }
+#pragma clang loop unroll(disable)
+  for (int j = wave; j < n_tiles; j += 2 * NW) {
+    step(j, kA, kB, v0, v1);
+    if (j + NW < n_tiles) step(j + NW, kB, kA, v1, v0);
+  }
+
+  // Merge.  Each wave parks (m, l) and its o rows in LDS (o columns XOR-
+  // swizzled by the row so that rows at one column fall in distinct banks);
+  // then wave w combines columns [w D/NW, (w+1) D/NW) of all 32 rows.
+  const float l = halfwave_sum(lpart.value());
+  __syncthreads();   // every wave is done with its V buffers
+  const int sw = (n & 15) << 2;
+  {
+    float* ob = (float*)(n < 16 ? v0 : v1) + (n & 15) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = db * 32 + 8 * i4 + 4 * g;
+        *(f32x4*)(ob + (col ^ sw)) = f32x4{oacc[db][4 * i4], oacc[db][4 * i4 + 1],
+                                           oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3]};
+      }
+    if (g == 0) {
+      sML[(wave * 32 + n) * 2] = m_ref;
+      sML[(wave * 32 + n) * 2 + 1] = l;
+    }
+  }
+  __syncthreads();
+  constexpr int CL = D / NW / 2;   // output columns per lane
+  float mw[NW], wt[NW];
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mw[w] = sML[(w * 32 + n) * 2];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wt[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - M);
+    L += wt[w] * sML[(w * 32 + n) * 2 + 1];
+  }
+  const int c0 = wave * (D / NW) + g * CL;
+  float acc[CL];
+#pragma unroll
+  for (int k = 0; k < CL; ++k) acc[k] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float* ob = (const float*)(n < 16 ? sV0 : sV1) + w * VBUF / 2 + (n & 15) * D;
+#pragma unroll
+    for (int k = 0; k < CL; k += 4) {
+      const f32x4 x = *(const f32x4*)(ob + ((c0 + k) ^ sw));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[k + e] = fmaf(wt[w], x[e], acc[k + e]);
+    }
+  }
+  if (row >= Sq) return;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* Orow = O + ((int64_t)bh * Sq + row) * D + c0;
+#pragma unroll
+  for (int k = 0; k < CL; k += 8) {
+    u32x4 w = {pack_bf16x2(acc[k] * inv, acc[k + 1] * inv), pack_bf16x2(acc[k + 2] * inv, acc[k + 3] * inv),
+               pack_bf16x2(acc[k + 4] * inv, acc[k + 5] * inv), pack_bf16x2(acc[k + 6] * inv, acc[k + 7] * inv)};
+    *(u32x4*)(Orow + k) = w;
+  }
+  if (LSE && wave == 0 && g == 0) LSE[(int64_t)bh * Sq + row] = (M + fast_log2(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int TPR, int NT, int KW, bool BIAS>
@@ -589,6 +833,25 @@ static hipError_t fwd_candidate(const FwdArgs* a, const void** fn) {
   return launch_fwd_bf16_k<D, CAUSAL, NW, BC, false, false>(*a);
 }
 
+// Key-split candidate: NW waves per 32-row query block.
+template <int D, bool CAUSAL, int NW>
+static hipError_t fwd_candidate_ks(const FwdArgs* a, const void** fn) {
+  if (fn) {
+    *fn = reinterpret_cast<const void*>(&fwd_bf16_ks_kernel<D, CAUSAL, NW>);
+    return hipSuccess;
+  }
+  const int n_qtiles = (a->Sq + 31) / 32;
+  const int items = n_qtiles * a->B * a->Hkv;
+  const int grid = (items + 7) / 8 * 8 * (a->Hq / a->Hkv);
+  timing_mark(a->stream, 0);
+  hipLaunchKernelGGL((fwd_bf16_ks_kernel<D, CAUSAL, NW>), dim3(grid), dim3(64 * NW), 0, a->stream,
+                     (const uint16_t*)a->q, (const uint16_t*)a->k, (const uint16_t*)a->v,
+                     (uint16_t*)a->o, a->lse, a->B * a->Hq, a->Hq, a->Hkv, a->Sq, a->Skv,
+                     a->scale * kLog2e, n_qtiles);
+  timing_mark(a->stream, 1);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
   // Must list the candidates of fwd_tile_candidates() in the same order.
@@ -598,6 +861,8 @@ static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
       case 1: return fwd_candidate<D, CAUSAL, 4, 32>(a, fn);
       case 2: return fwd_candidate<D, CAUSAL, 8, 64>(a, fn);
       case 3: return fwd_candidate<D, CAUSAL, 2, 64>(a, fn);
+      case 4: return fwd_candidate_ks<D, CAUSAL, 4>(a, fn);
+      case 5: return fwd_candidate_ks<D, CAUSAL, 2>(a, fn);
     }
   } else if constexpr (D == 128) {
     switch (idx) {
@@ -605,6 +870,8 @@ static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
       case 1: return fwd_candidate<D, CAUSAL, 4, 64>(a, fn);
       case 2: return fwd_candidate<D, CAUSAL, 8, 32>(a, fn);
       case 3: return fwd_candidate<D, CAUSAL, 8, 64>(a, fn);
+      case 4: return fwd_candidate_ks<D, CAUSAL, 4>(a, fn);
+      case 5: return fwd_candidate_ks<D, CAUSAL, 2>(a, fn);
     }
   } else {
     switch (idx) {

@@ -58,19 +58,20 @@ hipError_t fwd_candidate_fn(int d, bool causal, int idx, const void** fn);
 
 namespace {
 
+// nw < 0: the key-split kernel, |nw| waves on one 32-row query block.
 struct Cand {
   int nw, bc;
 };
 
 // Candidates per head dim, in the order of fwd_candidate_i in fwd.hip.
-const Cand kCand64[] = {{4, 64}, {4, 32}, {8, 64}, {2, 64}};
-const Cand kCand128[] = {{4, 32}, {4, 64}, {8, 32}, {8, 64}};
+const Cand kCand64[] = {{4, 64}, {4, 32}, {8, 64}, {2, 64}, {-4, 32}, {-2, 32}};
+const Cand kCand128[] = {{4, 32}, {4, 64}, {8, 32}, {8, 64}, {-4, 32}, {-2, 32}};
 const Cand kCand256[] = {{8, 32}, {4, 32}};
 
 int candidates(int d, const Cand** out) {
   switch (d) {
-    case 64: *out = kCand64; return 4;
-    case 128: *out = kCand128; return 4;
+    case 64: *out = kCand64; return 6;
+    case 128: *out = kCand128; return 6;
     case 256: *out = kCand256; return 2;
   }
   *out = nullptr;
@@ -89,6 +90,9 @@ constexpr double kPrologueBytesPerCycle = 10.0;   // its Q rows and first K/V ti
                                                  // compute unit's share of HBM
 constexpr double kEpilogue = 400.0;      // O and LSE stores
 constexpr double kLaunchUs = 4.0;        // launch and first-wave latency
+constexpr double kKsFillPerD = 16.0;     // key split: a wave's own K/V tile per column
+constexpr double kKsPrologue = 2400.0;   // key split: first-transfer latency
+constexpr double kKsMerge = 3000.0;      // key split: the states' merge through LDS
 
 // Workgroups per compute unit of candidate (d, causal, idx), from the
 // runtime's occupancy calculator (registers and LDS of the compiled kernel).
@@ -114,7 +118,50 @@ struct Shape {
   int d, causal, B, Hq, Hkv, Sq, Skv;
 };
 
+// Key-split candidate (|nw| waves on one 32-row query block, each with its
+// own tiles and state, merged at the end).  A wave moves its whole tile
+// (kKsFillPerD D cycles, no sharing), reads only V from LDS and has no
+// barrier; its workgroup takes as long as its busiest wave, ceil(n_t / NW)
+// tiles, plus the merge.  Every K/V tile is fetched once per wave instead of
+// once per workgroup, so the candidate only runs where the plain kernels
+// leave compute units idle: at most one 32-row query block per compute unit.
+double estimate_ks_us(const Shape& s, int NW, int occ, int cus) {
+  const int D = s.d, BC = 32;
+  const int off = s.Skv - s.Sq;
+  const int n_qt = (s.Sq + 31) / 32;
+  const int64_t n_wg = (int64_t)n_qt * s.B * s.Hq;
+  if (n_wg > cus) return INFINITY;
+  const double per_cu = std::min<double>(occ, (double)n_wg / cus);
+  const double w = std::max(1.0, per_cu * NW / 4.0);
+  const double O = w < 1.5 ? 0.0 : w < 2.5 ? kOverlap2 : kOverlap3;
+  const double tile = BC * D / 8.0 + kValuPer32 + 2.0 * BC * D / kLdsPerSimd - O + kKsFillPerD * D;
+  const double hide = std::max(1.0, per_cu);
+  const double pro = kKsPrologue + (32.0 * D * 2.0 + 4.0 * BC * D) / kPrologueBytesPerCycle;
+  std::vector<double> dur(n_qt);
+  for (int t = 0; t < n_qt; ++t) {
+    const int qt = s.causal ? n_qt - 1 - t : t;
+    const int last = std::min(qt * 32 + 32, s.Sq) - 1;
+    const int kv_end = s.causal ? std::max(0, std::min(s.Skv, last + off + 1)) : s.Skv;
+    const int n_t = (kv_end + BC - 1) / BC;
+    dur[t] = (n_t + NW - 1) / NW * tile + kKsMerge + (pro + kEpilogue) / hide;
+  }
+  const double machines_per_cu = NW >= 4 ? 1.0 : 4.0 / NW;
+  const int64_t machines = std::max<int64_t>(1, (int64_t)(cus * machines_per_cu));
+  std::priority_queue<double, std::vector<double>, std::greater<double>> freeat;
+  for (int64_t m = 0; m < std::min<int64_t>(machines, n_wg); ++m) freeat.push(0.0);
+  double makespan = 0.0;
+  for (int t = 0; t < n_qt; ++t)
+    for (int64_t j = 0; j < (int64_t)s.B * s.Hq; ++j) {
+      const double t1 = freeat.top() + dur[t];
+      freeat.pop();
+      makespan = std::max(makespan, t1);
+      freeat.push(t1);
+    }
+  return makespan / (kClockGHz * 1e3) + kLaunchUs;
+}
+
 double estimate_us(const Shape& s, Cand c, int occ, int cus) {
+  if (c.nw < 0) return estimate_ks_us(s, -c.nw, occ, cus);
   const int D = s.d, NW = c.nw, BC = c.bc, BR = 32 * NW;
   const int off = s.Skv - s.Sq;
   const int n_qt = (s.Sq + BR - 1) / BR;
@@ -198,7 +245,7 @@ int fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, in
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
-    const double t = estimate_us(s, cs[i], occupancy(d, causal != 0, i, cs[i].nw), cus);
+    const double t = estimate_us(s, cs[i], occupancy(d, causal != 0, i, abs(cs[i].nw)), cus);
     if (i < cap) {
       if (nw) nw[i] = cs[i].nw;
       if (bc) bc[i] = cs[i].bc;

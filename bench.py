@@ -792,6 +792,7 @@ TILE_SHAPES_VAL = [
     (2, 24, 24, 2048, 64, True),
     (16, 16, 16, 512, 128, True),
     (1, 64, 8, 6144, 128, True),
+    (1, 8, 2, 512, 64, True),
 ]
 
 

@@ -176,13 +176,16 @@ def test_decode_noalloc_validation():
 
 
 def test_fwd_tile_entry_points():
-    """Tile override: exactly one of (nw, bc) zero, or a negative value, is
-    rejected; plan: unsupported head dims and invalid shapes list nothing
-    (both checks happen before any device query)."""
+    """Tile override: exactly one of (nw, bc) zero, or a negative bc, is
+    rejected (a negative nw names a key-split candidate); plan: unsupported
+    head dims and invalid shapes list nothing (both checks happen before any
+    device query)."""
     L = aos.lib()
     assert L.attn_fwd_tile_override(4, 0) == VALUE
     assert L.attn_fwd_tile_override(0, 32) == VALUE
     assert L.attn_fwd_tile_override(-4, -32) == VALUE
+    assert L.attn_fwd_tile_override(4, -32) == VALUE
+    assert L.attn_fwd_tile_override(-4, 32) == 0
     assert L.attn_fwd_tile_override(0, 0) == 0
     assert aos.attn_fwd_tile_plan(80, True, 1, 1, 1, 64, 64) == (None, [])
     assert aos.attn_fwd_tile_plan(128, True, 1, 3, 2, 64, 64) == (None, [])

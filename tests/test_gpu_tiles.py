@@ -15,7 +15,8 @@ from tests.gpu_util import TOL_LSE, TOL_O, assert_close, inputs, note
 
 pytestmark = pytest.mark.gpu
 
-CANDS = {64: [(4, 64), (4, 32), (8, 64), (2, 64)], 128: [(4, 32), (4, 64), (8, 32), (8, 64)],
+CANDS = {64: [(4, 64), (4, 32), (8, 64), (2, 64), (-4, 32), (-2, 32)],
+         128: [(4, 32), (4, 64), (8, 32), (8, 64), (-4, 32), (-2, 32)],
          256: [(8, 32), (4, 32)]}
 # (B, Hq, Hkv, Sq, Skv, causal): ragged tails, grouped heads, Sq < Skv.
 SHAPES = [(1, 4, 2, 300, 300, True), (2, 2, 1, 77, 333, False), (1, 2, 2, 200, 460, True)]
@@ -26,8 +27,24 @@ def test_plan_lists_the_compiled_candidates(d):
     pick, cands = aos.attn_fwd_tile_plan(d, True, 4, 16, 16, 2048, 2048)
     assert [(c["nw"], c["bc"]) for c in cands] == CANDS[d]
     assert 0 <= pick < len(cands)
-    assert all(c["est_us"] > 0 and math.isfinite(c["est_us"]) for c in cands)
-    assert pick == min(range(len(cands)), key=lambda i: cands[i]["est_us"])
+    # The key-split candidates apply only to grids of at most one 32-row
+    # query block per compute unit; every plain candidate has an estimate.
+    for c in cands:
+        if c["nw"] > 0:
+            assert c["est_us"] > 0 and math.isfinite(c["est_us"])
+        else:
+            assert c["est_us"] is None
+    est = [c["est_us"] if c["est_us"] is not None else math.inf for c in cands]
+    assert pick == min(range(len(cands)), key=lambda i: est[i])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_plan_key_split_on_a_tiny_grid(d):
+    # 8 query blocks x 8 heads: 64 workgroups of the key-split kernel, far
+    # fewer than compute units; it gets an estimate there.
+    pick, cands = aos.attn_fwd_tile_plan(d, False, 1, 8, 8, 256, 256)
+    ks = [c for c in cands if c["nw"] < 0]
+    assert ks and all(c["est_us"] is not None and c["est_us"] > 0 for c in ks)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
