@@ -168,7 +168,8 @@ attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
   st = check_alias(outs, 2, ins, 4);
   if (st != ATTN_OK) return st;
   attn::FwdArgs a{dtype, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0,
-                  window > 0 ? window : 0, bias, bias_sb, bias_sh, scale, (hipStream_t)stream};
+                  window > 0 && window < Skv ? window : 0, bias, bias_sb, bias_sh, scale,
+                  (hipStream_t)stream};
   return hip_status(attn::launch_fwd(a));
 }
 
@@ -362,7 +363,7 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
   attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
-                  causal ? 1 : 0, window > 0 ? window : 0, bias, bias_sb, bias_sh, scale,
+                  causal ? 1 : 0, window > 0 && window < Skv ? window : 0, bias, bias_sb, bias_sh, scale,
                   (float*)workspace, (hipStream_t)stream};
   return hip_status(attn::launch_bwd(a));
 }

@@ -100,7 +100,8 @@ int attn_supports(int dtype, int entry, int d);
  *   causal != 0: key j allowed for query i iff j <= i + (Skv - Sq);
  *   window > 0 (causal only, else ATTN_ERR_VALUE): also j > i + (Skv - Sq)
  *   - window, a sliding window of `window` keys ending at the diagonal;
- *   window <= 0: no window;
+ *   window <= 0: no window; window >= Skv masks no key the causal mask
+ *   allows and runs as the plain causal call (the same kernels and bits);
  *   bias (may be NULL): float32 values added to the scaled scores,
  *   bias[b * bias_sb + h * bias_sh + i * Skv + j] for query head h (strides
  *   in elements, 0 to broadcast over batch or heads), any real or -inf; the
