@@ -334,6 +334,44 @@ __device__ __forceinline__ u32x4 tr_col8(const uint16_t* rows, const int* off, i
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Stores a wave's transposed accumulator X^T (lane n, g of the 32-row block:
+// row n; 32-column block db: the 16 values at columns 32 db + acc_row(i, g))
+// times mul (per row) as bf16 rows dst[r * D + c], r < nrows, through the
+// wave's LDS region of 32 x DC bf16, DC columns per pass.  Each lane writes
+// its 8-byte pieces to LDS, then reads back whole 16-byte chunks so that the
+// global stores cover consecutive columns of a row: 16 lanes write 256
+// contiguous bytes, where the direct stores of the accumulator layout put 8
+// bytes in each of 32 rows per instruction.  Chunk k of region row r sits at
+// chunk k ^ swz(r) (swz by r for 256-byte rows, r / 2 for 128-byte rows), so
+// the 8-byte writes of 32 rows and the 16-byte reads of a row fall in
+// distinct banks (two lanes per bank at most).
+template <int D, int DC, int NDB>
+__device__ __forceinline__ void store_rows_lds(uint16_t* dst, int nrows, const f32x16* acc,
+                                               float mul, uint16_t* region, int lane) {
+  constexpr int CPR = DC / 8;   // 16-byte chunks per region row
+  static_assert(DC == 64 || DC == 128 || DC == 256, "region width");
+  const int n = lane & 31, g = lane >> 5;
+  auto swz = [](int r) { return DC == 64 ? (r >> 1) & 7 : r & 15; };
+#pragma unroll
+  for (int p = 0; p < D / DC; ++p) {
+#pragma unroll
+    for (int db = p * DC / 32; db < (p + 1) * DC / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int k = (db - p * DC / 32) * 4 + i4;
+        const u32x2 w = {pack_bf16x2(acc[db][4 * i4] * mul, acc[db][4 * i4 + 1] * mul),
+                         pack_bf16x2(acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul)};
+        *(u32x2*)(region + n * DC + 8 * (k ^ swz(n)) + 4 * g) = w;
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int r = it * (64 / CPR) + lane / CPR, k = lane % CPR;
+      const u32x4 v = *(const u32x4*)(region + r * DC + 8 * (k ^ swz(r)));
+      if (r < nrows) *(u32x4*)(dst + (int64_t)r * D + p * DC + 8 * k) = v;
+    }
+  }
+}
+
 // An empty statement that the compiler must assume rewrites the N per-lane
 // offsets in place.  At the top of a loop body it keeps the sums LDS base +
 // offset inside the body, where the constant base folds into the immediate

@@ -504,19 +504,19 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW>)) void fwd_bf16_kerne
   }
 
   const float l = halfwave_sum(lpart.value());
-  if (!valid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
-  uint16_t* Orow = O + ((int64_t)bh * Sq + row) * D;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = db * 32 + 8 * i4 + 4 * g;
-      u32x2 w = {pack_bf16x2(oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv),
-                 pack_bf16x2(oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv)};
-      *(u32x2*)(Orow + d0) = w;
-    }
-  if (LSE && g == 0) LSE[(int64_t)bh * Sq + row] = (m_ref + fast_log2(l)) * kLn2;
+  if (LSE && g == 0 && valid) LSE[(int64_t)bh * Sq + row] = (m_ref + fast_log2(l)) * kLn2;
+  // O through LDS (the tile buffers, free once every wave is past the last
+  // tile): wave w's region of 32 rows x DC columns.
+  constexpr int DC = (BC * D / (8 * NW)) < D ? BC * D / (8 * NW) : D;
+  constexpr int PER = BC * D / (32 * DC);   // regions per tile buffer
+  static_assert(PER >= 1 && NW <= 4 * PER, "O staging must fit the tile buffers");
+  wait_vmcnt0();   // the transfer issued by the last step (past the keys) has landed
+  lds_barrier();
+  const int a = wave / PER;
+  uint16_t* region = (a == 0 ? sK0 : a == 1 ? sK1 : a == 2 ? sV0 : sV1) + (wave % PER) * 32 * DC;
+  store_rows_lds<D, DC, NDB>(O + ((int64_t)bh * Sq + q0 + wave * 32) * D,
+                             min(32, Sq - (q0 + wave * 32)), oacc, inv, region, lane);
 }
 
 // ---------------------------------------------------------------------------
