@@ -76,8 +76,30 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    write_build_info()
     build_ceilings(verbose)
     return LIB
+
+
+BUILD_INFO = os.path.join(PKG, "libattn.buildinfo.json")
+
+
+def write_build_info() -> None:
+    """The toolchain and flags libattn.so was built with, next to it, so
+    that a run can record them without starting the compiler (a child
+    program started from a process that uses the GPU is not always
+    allowed)."""
+    import hashlib
+    import json
+    r = subprocess.run([hipcc(), "--version"], capture_output=True, text=True)
+    h = hashlib.sha256()
+    with open(LIB, "rb") as f:
+        h.update(f.read())
+    info = {"hipcc": [ln for ln in r.stdout.splitlines() if ln.strip()][:2],
+            "build_flags": [f.replace(ROOT, "<repo>") for f in device_flags()],
+            "per_file_flags": FILE_FLAGS, "libattn_sha256_16": h.hexdigest()[:16]}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
 
 
 CEIL_SRC = os.path.join(PKG, "ceilings", "ceilings.hip")

@@ -279,7 +279,6 @@ def run_conditions():
     host cores ("Compilers and Kernels", section "Operating the
     compiler-kernel boundary": pin architecture, runtime, toolchain and
     flags)."""
-    import subprocess
     import torch
     from attention_online_softmax_amd import build as B
     from attention_online_softmax_amd.binding import LIB_PATH
@@ -290,20 +289,24 @@ def run_conditions():
             rocm_version = f.read().strip()
     except OSError:
         rocm_version = None
+    # The toolchain and flags come from the build's own record (no compiler
+    # is started from this process); the library's hash is taken here.
     try:
-        r = subprocess.run([B.hipcc(), "--version"], capture_output=True, text=True, timeout=60)
-        hipcc_version = [ln for ln in r.stdout.splitlines() if ln.strip()][:2]
-    except Exception:
-        hipcc_version = None
+        with open(B.BUILD_INFO) as f:
+            info = json.load(f)
+    except (OSError, ValueError):
+        info = {}
     h = hashlib.sha256()
     with open(LIB_PATH, "rb") as f:
         h.update(f.read())
+    lib_hash = h.hexdigest()[:16]
     return {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": rocm_version,
             "hip_runtime": torch.version.hip, "torch": torch.__version__,
-            "hipcc": hipcc_version,
-            "build_flags": [f.replace(ROOT, "<repo>") for f in B.device_flags()],
-            "per_file_flags": B.FILE_FLAGS, "libattn_sha256_16": h.hexdigest()[:16],
+            "hipcc": info.get("hipcc"),
+            "build_flags": info.get("build_flags"), "per_file_flags": info.get("per_file_flags"),
+            "libattn_sha256_16": lib_hash,
+            "build_info_matches_library": info.get("libattn_sha256_16") == lib_hash,
             "cpu_model": cpu_model(), "host_affinity_cores": len(os.sched_getaffinity(0)),
             "blas_threads": blas_threads()}
 
