@@ -158,6 +158,33 @@ def test_fwd_hidden(case):
     check(to_f64(o), lse.cpu().numpy(), O, L, tol_o, tol_l, f"fwd {case}")
 
 
+# The bf16 forward's tiles forced one by one on every kind: the key-split
+# kernel (|nw| waves sharing one 32-row block and splitting its keys, states
+# merged at the end) and a plain tile.  The estimate picks between them by
+# grid size, so neither family's hidden-semantics coverage is left to it.
+FWD_TILES = [(d, causal, kind, nw, bc) for d in (64, 128) for causal in (True, False)
+             for kind in KINDS for nw, bc in ((-4, 32), (-2, 32), (4, 32))]
+
+
+@pytest.mark.parametrize("case", FWD_TILES, ids=ids)
+def test_fwd_hidden_forced_tile(case):
+    d, causal, kind, nw, bc = case
+    B, Hq, Hkv, Sq, Skv = 1, 2, 1, 300, 333
+    cpu, scale = hostile(kind, B, Hq, Hkv, Sq, Skv, d, "bf16", 7300 + d + 2 * causal)
+    ref = {k: to_f64(v) for k, v in cpu.items()}
+    dev = {k: v.cuda() for k, v in cpu.items()}
+    note(f"fwd hidden forced tile {case}")
+    aos.attn_fwd_tile_override(nw, bc)
+    try:
+        o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
+        torch.cuda.synchronize()
+    finally:
+        aos.attn_fwd_tile_override(0, 0)
+    O, L = oracle.attention_ref(ref["q"], ref["k"], ref["v"], causal, scale)
+    tol_o, tol_l, _ = tols(kind, "bf16", ref, scale, d)
+    check(to_f64(o), lse.cpu().numpy(), O, L, tol_o, tol_l, f"fwd forced {case}")
+
+
 # A 256-thread-workgroup fp32 grid (32 columns per lane) and bf16 grids with
 # several workgroups per head, for the kinds that stress the softmax.
 FWD_LARGE = [(dt, d, kind) for dt, d in (("f32", 64), ("bf16", 128), ("bf16", 64))
