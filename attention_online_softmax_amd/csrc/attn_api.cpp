@@ -150,8 +150,6 @@ attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
   if (window > 0 && !causal) return ATTN_ERR_VALUE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   if (!fwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
-  // bf16 with a bias: d <= 128 (the d256 kernel has no registers to spare).
-  if (bias && dtype == ATTN_BF16 && d > 128) return ATTN_ERR_UNSUPPORTED;
   // A forced tile shape (attn_fwd_tile_override) must be compiled for d.
   if (dtype == ATTN_BF16 && !attn::fwd_tile_override_ok(d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;

@@ -241,12 +241,13 @@ constexpr float kLazyBound = 256.f;   // 2^kLazy
 // a per-tile time estimate (fwd_tiles.cpp).  The bias path adds its values
 // tile by tile for 32 keys.  Two waves per SIMD must fit (at most 256
 // registers), except for the eight-wave d256 kernel, which is the only
-// workgroup on its compute unit.
-template <int D, int NW>
-constexpr int kFwdMinWaves = (NW == 8 && D >= 256) ? 1 : 2;
+// workgroup on its compute unit, and the d256 bias kernel, whose bias
+// values need registers beyond 256 (one wave per SIMD, up to 512).
+template <int D, int NW, bool BIAS>
+constexpr int kFwdMinWaves = (D >= 256 && (NW == 8 || BIAS)) ? 1 : 2;
 
 template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS>
-__global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW>)) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
@@ -905,21 +906,18 @@ static hipError_t launch_fwd_bf16_w(const FwdArgs& a) {
     const int idx = fwd_pick_candidate(a);
     return fwd_candidate_i<D, CAUSAL>(idx, &a, nullptr);
   } else {
-    constexpr int NW = D >= 256 ? 8 : 4;
+    // d256 with a bias: four waves at one per SIMD (the bias values of a
+    // tile need registers beyond the eight-wave kernel's 256).
+    constexpr int NW = (D >= 256 && !BIAS) ? 8 : 4;
     constexpr int BC = (D == 64 && !BIAS) ? 64 : 32;
     return launch_fwd_bf16_k<D, CAUSAL, NW, BC, WIN, BIAS>(a);
   }
 }
 
-// An additive bias is a template parameter too (d <= 128: the d256 kernel
-// has no registers to spare for the bias of its tiles).
+// An additive bias is a template parameter too.
 template <int D, bool CAUSAL, bool WIN>
 static hipError_t launch_fwd_bf16_b(const FwdArgs& a) {
-  if constexpr (D <= 128) {
-    if (a.bias) return launch_fwd_bf16_w<D, CAUSAL, WIN, true>(a);
-  } else {
-    if (a.bias) return hipErrorInvalidValue;
-  }
+  if (a.bias) return launch_fwd_bf16_w<D, CAUSAL, WIN, true>(a);
   return launch_fwd_bf16_w<D, CAUSAL, WIN, false>(a);
 }
 

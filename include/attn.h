@@ -106,8 +106,7 @@ int attn_supports(int dtype, int entry, int d);
  *   bias[b * bias_sb + h * bias_sh + i * Skv + j] for query head h (strides
  *   in elements, 0 to broadcast over batch or heads), any real or -inf; the
  *   pointer 16-byte aligned and Skv, bias_sb, bias_sh multiples of 4 (else
- *   ATTN_ERR_ALIGN), strides >= 0 (else ATTN_ERR_VALUE); bf16 with a bias
- *   supports d in {64, 128} (else ATTN_ERR_UNSUPPORTED).  A row whose every
+ *   ATTN_ERR_ALIGN), strides >= 0 (else ATTN_ERR_VALUE).  A row whose every
  *   key is masked gets O = 0 and lse = -inf.
  */
 attn_status attn_fwd(int dtype, const void* q, const void* k, const void* v,

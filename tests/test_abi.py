@@ -106,7 +106,6 @@ def test_fwd_validation():
     assert fwd(**base, bias=bias + 4) == ALIGN
     assert fwd(**base, bias=bias, sb=6) == ALIGN
     assert fwd(**base, bias=bias, sh=-4) == VALUE
-    assert fwd(**dict(base, d=256), bias=bias) == UNSUP      # bf16 d256 takes no bias
     assert fwd(**base, bias=p["o"]) == ALIAS                 # the bias overlaps an output
     assert fwd(**base, d=96) == UNSUP
     assert fwd(**base, dt=5) == UNSUP

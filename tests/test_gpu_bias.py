@@ -43,6 +43,9 @@ FWD_CASES = [
     (1, 2, 2, 130, 132, 128, True, 40, "full", "bf16"),
     (1, 2, 1, 50, 52, 64, True, 0, "full", "f32"),
     (2, 2, 2, 33, 36, 256, False, 0, "batch1", "f32"),
+    (1, 2, 1, 100, 128, 256, True, 0, "full", "bf16"),
+    (2, 2, 2, 64, 96, 256, False, 0, "head1", "bf16"),
+    (1, 2, 2, 130, 132, 256, True, 40, "shared", "bf16"),
 ]
 
 

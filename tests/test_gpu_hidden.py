@@ -208,7 +208,8 @@ def test_fwd_hidden_large_grid(case):
 
 # Additive bias and sliding window with zero and negative scales: the bias
 # alone then decides the weights (zero scale), or the scores change sign.
-BIAS_CASES = [(dt, d, kind, window) for dt, d in (("f32", 64), ("bf16", 64), ("bf16", 128))
+BIAS_CASES = [(dt, d, kind, window) for dt, d in (("f32", 64), ("bf16", 64), ("bf16", 128),
+                                                  ("bf16", 256))
               for kind in ("zero_scale", "neg_scale", "negzero_scale") for window in (0, 50)]
 
 
