@@ -38,7 +38,8 @@ bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
 
 bool fwd_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
 bool decode_d_ok(int dtype, int d) { return dtype_ok(dtype) && (d == 64 || d == 128 || d == 256); }
-bool bwd_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
+bool bwd_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128 || d == 256); }
+bool bwd_fused_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
 bool paged_d_ok(int dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
 
 // Per-head element counts must stay within 32-bit index arithmetic.
@@ -134,7 +135,7 @@ int attn_supports(int dtype, int entry, int d) {
     case 1: return decode_d_ok(dtype, d);
     case 2: return bwd_d_ok(dtype, d);
     case 3: return paged_d_ok(dtype, d);
-    case 4: return bwd_d_ok(dtype, d);
+    case 4: return bwd_fused_d_ok(dtype, d);
   }
   return 0;
 }
@@ -383,7 +384,7 @@ attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* 
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   // The (D, nl) pairs are addressed with 32-bit byte offsets.
   if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
-  if (!bwd_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
+  if (!bwd_fused_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
   if (!workspace) return ATTN_ERR_WORKSPACE;
   const size_t ws_need = attn_bwd_fused_workspace_bytes(B, Hq, Sq, d);

@@ -91,6 +91,7 @@ bool fwd_tile_override_ok(int d);
 void fwd_tile_set_override(int nw, int bc);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_bwd_d256(const BwdArgs& a);   // d = 256 (bwd256.hip)
 // Fused variant (no window or bias): ws holds the (D, nl) pairs, then from
 // bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].
 hipError_t launch_bwd_fused(const BwdArgs& a);

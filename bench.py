@@ -46,7 +46,7 @@ KERNELS = {
     "decode": ["decode_split_kernel", "decode_combine_kernel"],
 }
 SOURCES = {"fwd_bf16_kernel": "fwd.hip",
-           "bwd_dkdv_kernel": "bwd.hip", "bwd_dq_kernel": "bwd.hip",
+           "bwd_dkdv_kernel": "bwd_kernels.h", "bwd_dq_kernel": "bwd_kernels.h",
            "decode_split_kernel": "decode.hip", "decode_combine_kernel": "decode.hip"}
 
 

@@ -239,7 +239,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
  * causal, window and bias as in attn_fwd (the same mask as the forward
  * call; no gradient is formed for the bias).  Rows with lse = -inf (no
  * allowed key) contribute nothing.
- * Supported: bf16 with d in {64, 128}.
+ * Supported: bf16 with d in {64, 128, 256} (d = 256 at one wave per SIMD).
  */
 attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v,
                      const void* o, const void* d_o, const float* lse,

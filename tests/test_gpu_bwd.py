@@ -21,6 +21,10 @@ CASES = [
     (1, 1, 1, 1, 1, 64, False),
     (1, 8, 1, 64, 64, 64, True),
     (1, 2, 2, 33, 2000, 128, True),
+    (1, 2, 2, 200, 200, 256, True),
+    (1, 4, 2, 130, 300, 256, True),
+    (1, 2, 2, 97, 161, 256, False),
+    (1, 8, 1, 64, 64, 256, True),
 ]
 
 

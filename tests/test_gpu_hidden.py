@@ -289,10 +289,11 @@ def test_decode_paged_hidden(case):
 
 
 # ---------------------------------------------------------------------------
-# Backward (two-kernel and fused), bf16 d64 and d128.
+# Backward (two-kernel and fused), bf16 d64 and d128; the two-kernel one
+# also at d256.
 # ---------------------------------------------------------------------------
-BWD = [(fused, d, causal, kind) for fused in (False, True) for d in (64, 128)
-       for causal in (True, False) for kind in KINDS]
+BWD = [(fused, d, causal, kind) for fused in (False, True) for d in (64, 128, 256)
+       for causal in (True, False) for kind in KINDS if not (fused and d == 256)]
 
 
 @pytest.mark.parametrize("case", BWD, ids=lambda c: ("fused_" if c[0] else "") + ids(c[1:]))
