@@ -78,9 +78,9 @@ def lib():
                                  i, i, i, i, i, i, i, f, vp, sz, vp]
     ip, fp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)
     L.attn_fwd_tile_plan.restype = i
-    L.attn_fwd_tile_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, fp, ip]
+    L.attn_fwd_tile_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, ip, fp, ip]
     L.attn_fwd_tile_override.restype = i
-    L.attn_fwd_tile_override.argtypes = [i, i]
+    L.attn_fwd_tile_override.argtypes = [i, i, i]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -114,24 +114,28 @@ def attn_set_timing_events(events):
 
 def attn_fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv):
     """The bf16 forward's tile candidates for a shape: a list of
-    {"nw", "bc", "est_us"} and the index the estimate picks (None, [] for an
-    unsupported head dim or shape).  nw < 0 is the key-split kernel (|nw|
-    waves on one 32-row query block); est_us is None where a candidate does
-    not apply to the shape."""
+    {"nw", "bc", "split", "est_us"} and the index the estimate picks (None, []
+    for an unsupported head dim or shape).  nw waves in `split` key groups,
+    32 nw / split query rows per workgroup (split = nw: the key-split kernel
+    on one 32-row block); est_us is None where a candidate does not apply
+    to the shape."""
     cap = 16
-    nw, bc = (ctypes.c_int * cap)(), (ctypes.c_int * cap)()
+    nw, bc, sp = (ctypes.c_int * cap)(), (ctypes.c_int * cap)(), (ctypes.c_int * cap)()
     est, pick = (ctypes.c_float * cap)(), ctypes.c_int(-1)
-    n = lib().attn_fwd_tile_plan(int(d), int(bool(causal)), B, Hq, Hkv, Sq, Skv, cap, nw, bc, est,
-                                 ctypes.byref(pick))
-    cands = [{"nw": nw[i], "bc": bc[i], "est_us": est[i] if math.isfinite(est[i]) else None}
-             for i in range(min(n, cap))]
+    n = lib().attn_fwd_tile_plan(int(d), int(bool(causal)), B, Hq, Hkv, Sq, Skv, cap, nw, bc, sp,
+                                 est, ctypes.byref(pick))
+    cands = [{"nw": nw[i], "bc": bc[i], "split": sp[i],
+              "est_us": est[i] if math.isfinite(est[i]) else None} for i in range(min(n, cap))]
     return (pick.value if n else None), cands
 
 
-def attn_fwd_tile_override(nw=0, bc=0):
-    """Force (waves per workgroup, keys per tile) on this thread's later bf16
-    forward calls without window or bias; (0, 0) returns to the estimate."""
-    st = lib().attn_fwd_tile_override(int(nw), int(bc))
+def attn_fwd_tile_override(nw=0, bc=0, split=1):
+    """Force (waves per workgroup, keys per tile, key groups) on this
+    thread's later bf16 forward calls without window or bias; nw = bc = 0
+    returns to the estimate."""
+    if nw == 0 and bc == 0:
+        split = 0
+    st = lib().attn_fwd_tile_override(int(nw), int(bc), int(split))
     if st:
         raise AttnError(st, "attn_fwd_tile_override")
 

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxSplits = 256;
 
 struct Span {
@@ -108,18 +108,19 @@ const char* attn_status_str(int s) {
   return "unknown status";
 }
 
-attn_status attn_fwd_tile_override(int nw, int bc) {
-  if ((nw == 0) != (bc == 0) || bc < 0) return ATTN_ERR_VALUE;
-  attn::fwd_tile_set_override(nw, bc);
+attn_status attn_fwd_tile_override(int nw, int bc, int split) {
+  const bool none = nw == 0 && bc == 0 && split == 0;
+  if (!none && (nw <= 0 || bc <= 0 || split <= 0 || nw % split != 0)) return ATTN_ERR_VALUE;
+  attn::fwd_tile_set_override(nw, bc, split);
   return ATTN_OK;
 }
 
 int attn_fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap,
-                       int* nw, int* bc, float* est_us, int* pick) {
+                       int* nw, int* bc, int* split, float* est_us, int* pick) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || cap < 0)
     return 0;
   if (causal && Sq > Skv) return 0;
-  return attn::fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv, cap, nw, bc, est_us, pick);
+  return attn::fwd_tile_plan(d, causal, B, Hq, Hkv, Sq, Skv, cap, nw, bc, split, est_us, pick);
 }
 
 attn_status attn_set_timing_events(void* const* events, int n) {

@@ -246,24 +246,35 @@ constexpr float kLazyBound = 256.f;   // 2^kLazy
 template <int D, int NW, bool BIAS>
 constexpr int kFwdMinWaves = (D >= 256 && (NW == 8 || BIAS)) ? 1 : 2;
 
-template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS>
+// SPLIT = 2: the workgroup's waves form two groups of NW/2, each with the
+// same NW/2 32-row query blocks; group h takes the key tiles j0 + h,
+// j0 + h + 2, ... (each group loads its own tiles), and the second group's
+// (m, l, o) of every row is merged into the first's at the end by the
+// online-softmax monoid ("Tang, a compiler that derives GPU kernels and
+// bounds how fast they can run", Abstract).  A causal grid with few query
+// tiles per compute unit then takes half the key steps per workgroup.
+template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS, int SPLIT = 1>
 __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int Hq, int Hkv, int Sq, int Skv,
     int window, const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale_log2,
     int n_qtiles) {
   static_assert(!BIAS || BC == 32, "the bias path works on 32-key tiles");
-  constexpr int BR = 32 * NW;    // query rows per workgroup (32 per wave)
+  static_assert(SPLIT == 1 || (SPLIT == 2 && NW == 4 && BC >= 32 && !WIN && !BIAS),
+                "key halves: two groups of two waves, plain calls");
+  constexpr int NQ = NW / SPLIT; // 32-row query blocks per workgroup
+  constexpr int BR = 32 * NQ;    // query rows per workgroup
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T k-steps)
   constexpr int NDB = D / 32;    // 32-wide d blocks (PV output blocks)
   // Two tile buffers per tensor, as separate variables: the compiler can
   // then see which buffer each transfer writes and each read reads, and
   // does not wait for the transfer into one before reading the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
+  // With SPLIT = 2 each buffer holds one tile per key group.
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[SPLIT * BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[SPLIT * BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[SPLIT * BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[SPLIT * BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -285,14 +296,17 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16
   const int qtile = CAUSAL ? (n_qtiles - 1 - t) : t;
   const int off = Skv - Sq;
   const int q0 = qtile * BR;
-  const int row = q0 + wave * 32 + n;
+  const int qb = SPLIT == 1 ? wave : wave % NQ;   // the wave's 32-row block
+  const int kg = SPLIT == 1 ? 0 : wave / NQ;      // its key group
+  const int kgo = kg * BC * D;                    // its tiles' offset in a buffer
+  const int row = q0 + qb * 32 + n;
   const bool valid = row < Sq;
 
   const uint16_t* Qh = Q + (int64_t)bh * Sq * D;
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
-  TileDma<D, BC, NW> dma;
-  dma.init(wave, lane);
+  TileDma<D, BC, NQ> dma;   // a key group's tile, moved by its NQ waves
+  dma.init(qb, lane);
 
   const int last_row = min(q0 + BR, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
@@ -326,8 +340,8 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16
     qreg[c] = *(const u32x4*)(Qh + (int64_t)qrow * D + c * 16 + 8 * g);
     qreg[c] = (qreg[c] ^ qsign) & qkeep;
   }
-  dma.load(Kh, Skv, sK0, j0 * BC, wave);
-  dma.load(Vh, Skv, sV0, j0 * BC, wave);
+  dma.load(Kh, Skv, sK0 + kgo, (j0 + kg) * BC, qb);
+  dma.load(Vh, Skv, sV0 + kgo, (j0 + kg) * BC, qb);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -444,8 +458,8 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16
     // products of one wave with the softmax and LDS latency of another.
     // Tiles past the last key of this wave's rows are skipped.
     const int wave_kv_last =
-        CAUSAL ? min(Skv, min(q0 + wave * 32 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
-    const int wave_kv_first = win ? q0 + wave * 32 + off - window + 1 : 0;
+        CAUSAL ? min(Skv, min(q0 + qb * 32 + 31, Sq - 1) + off + 1) - 1 : Skv - 1;
+    const int wave_kv_first = win ? q0 + qb * 32 + off - window + 1 : 0;
     // Additive bias of this lane's query for the keys it holds: keys
     // k0 + 16c + 8g + 0..7 (c = 0, 1) in bv[2c], bv[2c + 1].  The next
     // tile's values are requested while the current tile is used.
@@ -467,13 +481,19 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16
     if constexpr (BIAS) load_bias(j0 * BC, bnext);
     f32x16 s[NKB];
     u32x4 p[NKB][2];
+    // Step j0 + SPLIT i: this wave's tile is j = the step's first tile plus
+    // its key group (past n_tiles for the second group of an odd count:
+    // skipped below, as tiles past the wave's keys are).
     auto step = [&](int j, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
+      j += kg;
+      cK += kgo;
+      cV += kgo;
       wait_vmcnt0();   // this wave's part of tile j has landed
       lds_barrier();   // ... and every wave's; tile j-1 is no longer read
       opaque_offsets<kRowOffs<D>>(k_off);
       opaque_offsets<kTrOffs<D>>(v_off);
-      dma.load(Kh, Skv, nK, (j + 1) * BC, wave);
-      dma.load(Vh, Skv, nV, (j + 1) * BC, wave);
+      dma.load(Kh, Skv, nK + kgo, (j + SPLIT) * BC, qb);
+      dma.load(Vh, Skv, nV + kgo, (j + SPLIT) * BC, qb);
       f32x4 bcur[4];
       if constexpr (BIAS) {
 #pragma unroll
@@ -498,15 +518,51 @@ __global__ __launch_bounds__(64 * NW, (kFwdMinWaves<D, NW, BIAS>)) void fwd_bf16
       pv(cV, p);
     };
 #pragma clang loop unroll(disable)
-    for (int j = j0; j < n_tiles; j += 2) {
+    for (int j = j0; j < n_tiles; j += 2 * SPLIT) {
       step(j, sK0, sV0, sK1, sV1);
-      if (j + 1 < n_tiles) step(j + 1, sK1, sV1, sK0, sV0);
+      if (j + SPLIT < n_tiles) step(j + SPLIT, sK1, sV1, sK0, sV0);
     }
   }
 
-  const float l = halfwave_sum(lpart.value());
+  float l = halfwave_sum(lpart.value());
+  if constexpr (SPLIT == 2) {
+    // The second key group parks its (m, l, o) in LDS at its lanes'
+    // positions; the first folds it into its own state (same rows, same
+    // lane layout) and alone stores O and LSE.  o of block qb: buffer sK0
+    // or sV0; m and l: past the O staging area of sK1 or sV1.
+    wait_vmcnt0();   // the transfer issued by the last step (past the keys) has landed
+    lds_barrier();
+    float* mo = (float*)(qb == 0 ? sK0 : sV0);
+    float* ml = (float*)((qb == 0 ? sK1 : sV1) + 32 * D);
+    if (kg == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mo[(db * 16 + i) * 64 + lane] = oacc[db][i];
+      ml[lane] = m_ref;
+      ml[64 + lane] = l;
+    }
+    lds_barrier();
+    if (kg == 1) return;   // past the workgroup's last barrier
+    const float m1 = ml[lane], l1 = ml[64 + lane];
+    const float M = fmaxf(m_ref, m1);
+    const float w0 = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - M);
+    const float w1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = fmaf(w1, mo[(db * 16 + i) * 64 + lane], w0 * oacc[db][i]);
+    l = fmaf(w1, l1, w0 * l);
+    m_ref = M;
+  }
   const float inv = l > 0.f ? 1.f / l : 0.f;   // a row with no allowed key: O = 0, LSE = -inf
   if (LSE && g == 0 && valid) LSE[(int64_t)bh * Sq + row] = (m_ref + fast_log2(l)) * kLn2;
+  if constexpr (SPLIT == 2) {
+    // O of block qb through the first 32 rows of sK1 or sV1.
+    store_rows_lds<D, D, NDB>(O + ((int64_t)bh * Sq + q0 + qb * 32) * D,
+                              min(32, Sq - (q0 + qb * 32)), oacc, inv, qb == 0 ? sK1 : sV1, lane);
+    return;
+  }
   // O through LDS (the tile buffers, free once every wave is past the last
   // tile): wave w's region of 32 rows x DC columns.
   constexpr int DC = (BC * D / (8 * NW)) < D ? BC * D / (8 * NW) : D;
@@ -806,16 +862,17 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a) {
 }
 
 // One bf16 forward launch with NW waves per workgroup and BC keys per tile.
-template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS>
+template <int D, bool CAUSAL, int NW, int BC, bool WIN, bool BIAS, int SPLIT = 1>
 static hipError_t launch_fwd_bf16_k(const FwdArgs& a) {
-  const int n_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
+  constexpr int BR = 32 * NW / SPLIT;   // query rows per workgroup
+  const int n_qtiles = (a.Sq + BR - 1) / BR;
   const int BH = a.B * a.Hq;
   timing_mark(a.stream, 0);
   // Items of (query tile, batch, key/value head) in groups of 8, one
   // workgroup per query head of each (see the kernel's work mapping).
   const int items = n_qtiles * a.B * a.Hkv;
   const int grid = (items + 7) / 8 * 8 * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, WIN, BIAS>), dim3(grid),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, WIN, BIAS, SPLIT>), dim3(grid),
                      dim3(64 * NW), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
                      a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
@@ -825,13 +882,13 @@ static hipError_t launch_fwd_bf16_k(const FwdArgs& a) {
 
 // Candidate (NW, BC) of the plain (no window, no bias) kernel: launch it, or
 // with fn != nullptr only report its function (for occupancy queries).
-template <int D, bool CAUSAL, int NW, int BC>
+template <int D, bool CAUSAL, int NW, int BC, int SPLIT = 1>
 static hipError_t fwd_candidate(const FwdArgs* a, const void** fn) {
   if (fn) {
-    *fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, NW, BC, false, false>);
+    *fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, NW, BC, false, false, SPLIT>);
     return hipSuccess;
   }
-  return launch_fwd_bf16_k<D, CAUSAL, NW, BC, false, false>(*a);
+  return launch_fwd_bf16_k<D, CAUSAL, NW, BC, false, false, SPLIT>(*a);
 }
 
 // Key-split candidate: NW waves per 32-row query block.
@@ -864,6 +921,7 @@ static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
       case 3: return fwd_candidate<D, CAUSAL, 2, 64>(a, fn);
       case 4: return fwd_candidate_ks<D, CAUSAL, 4>(a, fn);
       case 5: return fwd_candidate_ks<D, CAUSAL, 2>(a, fn);
+      case 6: return fwd_candidate<D, CAUSAL, 4, 64, 2>(a, fn);
     }
   } else if constexpr (D == 128) {
     switch (idx) {
@@ -873,6 +931,7 @@ static hipError_t fwd_candidate_i(int idx, const FwdArgs* a, const void** fn) {
       case 3: return fwd_candidate<D, CAUSAL, 8, 64>(a, fn);
       case 4: return fwd_candidate_ks<D, CAUSAL, 4>(a, fn);
       case 5: return fwd_candidate_ks<D, CAUSAL, 2>(a, fn);
+      case 6: return fwd_candidate<D, CAUSAL, 4, 32, 2>(a, fn);
     }
   } else {
     switch (idx) {

@@ -58,20 +58,24 @@ hipError_t fwd_candidate_fn(int d, bool causal, int idx, const void** fn);
 
 namespace {
 
-// nw < 0: the key-split kernel, |nw| waves on one 32-row query block.
+// nw waves per workgroup in `split` key groups of nw / split waves; group
+// g takes the bc-key tiles g, g + split, ...; 32 nw / split query rows per
+// workgroup.  split = nw is the key-split kernel (one 32-row block).
 struct Cand {
-  int nw, bc;
+  int nw, bc, split;
 };
 
 // Candidates per head dim, in the order of fwd_candidate_i in fwd.hip.
-const Cand kCand64[] = {{4, 64}, {4, 32}, {8, 64}, {2, 64}, {-4, 32}, {-2, 32}};
-const Cand kCand128[] = {{4, 32}, {4, 64}, {8, 32}, {8, 64}, {-4, 32}, {-2, 32}};
-const Cand kCand256[] = {{8, 32}, {4, 32}};
+const Cand kCand64[] = {{4, 64, 1}, {4, 32, 1}, {8, 64, 1}, {2, 64, 1},
+                        {4, 32, 4}, {2, 32, 2}, {4, 64, 2}};
+const Cand kCand128[] = {{4, 32, 1}, {4, 64, 1}, {8, 32, 1}, {8, 64, 1},
+                         {4, 32, 4}, {2, 32, 2}, {4, 32, 2}};
+const Cand kCand256[] = {{8, 32, 1}, {4, 32, 1}};
 
 int candidates(int d, const Cand** out) {
   switch (d) {
-    case 64: *out = kCand64; return 6;
-    case 128: *out = kCand128; return 6;
+    case 64: *out = kCand64; return 7;
+    case 128: *out = kCand128; return 7;
     case 256: *out = kCand256; return 2;
   }
   *out = nullptr;
@@ -93,6 +97,7 @@ constexpr double kLaunchUs = 4.0;        // launch and first-wave latency
 constexpr double kKsFillPerD = 16.0;     // key split: a wave's own K/V tile per column
 constexpr double kKsPrologue = 2400.0;   // key split: first-transfer latency
 constexpr double kKsMerge = 3000.0;      // key split: the states' merge through LDS
+constexpr double kSplitMerge = 1500.0;   // two key groups: the second's state merged into the first
 
 // Workgroups per compute unit of candidate (d, causal, idx), from the
 // runtime's occupancy calculator (registers and LDS of the compiled kernel).
@@ -161,8 +166,8 @@ double estimate_ks_us(const Shape& s, int NW, int occ, int cus) {
 }
 
 double estimate_us(const Shape& s, Cand c, int occ, int cus) {
-  if (c.nw < 0) return estimate_ks_us(s, -c.nw, occ, cus);
-  const int D = s.d, NW = c.nw, BC = c.bc, BR = 32 * NW;
+  if (c.split > 1 && c.split == c.nw) return estimate_ks_us(s, c.nw, occ, cus);
+  const int D = s.d, NW = c.nw, BC = c.bc, SP = c.split, NQ = NW / SP, BR = 32 * NQ;
   const int off = s.Skv - s.Sq;
   const int n_qt = (s.Sq + BR - 1) / BR;
   const int64_t n_wg = (int64_t)n_qt * s.B * s.Hq;
@@ -176,7 +181,8 @@ double estimate_us(const Shape& s, Cand c, int occ, int cus) {
   const double L = 4.0 * BC * D / kLdsPerSimd;
   const double O = (w < 1.5 ? 0.0 : w < 2.5 ? kOverlap2 : kOverlap3) * k32;
   const double busy_cost = M + V + L - O;
-  const double wait_cost = kFillPerD * D / NW * k32 + kSyncPerTile;
+  // A key group's tile is moved by its NQ waves.
+  const double wait_cost = kFillPerD * D / NQ * k32 + kSyncPerTile;
   const double hide = std::max(1.0, per_cu);
   const int step = NW > 4 ? 2 : 1;   // waves sharing one SIMD within a workgroup
   auto duration = [&](int qt) {
@@ -184,19 +190,23 @@ double estimate_us(const Shape& s, Cand c, int occ, int cus) {
     const int last = std::min(q0 + BR, s.Sq) - 1;
     const int kv_end = s.causal ? std::min(s.Skv, last + off + 1) : s.Skv;
     const int n_t = (kv_end + BC - 1) / BC;
+    const int n_steps = (n_t + SP - 1) / SP;   // every wave waits on every step
     double cyc = 0.0;
     for (int wv = 0; wv < NW; wv += step) {
       double simd = 0.0;
       for (int k = 0; k < step; ++k) {
-        const int r1 = std::min(q0 + 32 * (wv + k) + 31, s.Sq - 1);
+        const int w = wv + k, qb = w % NQ, kg = w / NQ;
+        const int r1 = std::min(q0 + 32 * qb + 31, s.Sq - 1);
         const int wk = s.causal ? std::max(0, std::min(s.Skv, r1 + off + 1)) : s.Skv;
-        const int busy = std::min(n_t, (wk + BC - 1) / BC);
-        simd += busy * busy_cost + n_t * wait_cost;
+        // The wave's tiles: kg, kg + SP, ... below its last key's tile.
+        const int nt_w = std::min(n_t, (wk + BC - 1) / BC);
+        const int busy = nt_w > kg ? (nt_w - kg + SP - 1) / SP : 0;
+        simd += busy * busy_cost + n_steps * wait_cost;
       }
       cyc = std::max(cyc, simd);
     }
     const double pro = kPrologue + (BR * D * 2.0 + 4.0 * BC * D) / kPrologueBytesPerCycle;
-    return cyc + (pro + kEpilogue) / hide;
+    return cyc + (SP > 1 ? kSplitMerge : 0.0) + (pro + kEpilogue) / hide;
   };
   std::vector<double> dur(n_qt);
   for (int t = 0; t < n_qt; ++t) dur[t] = duration(s.causal ? n_qt - 1 - t : t);
@@ -225,7 +235,7 @@ struct KeyHash {
   }
 };
 
-thread_local int t_override_nw = 0, t_override_bc = 0;
+thread_local int t_override_nw = 0, t_override_bc = 0, t_override_split = 0;
 
 int device_cus_cached() {
   static int cus = 0;
@@ -236,7 +246,7 @@ int device_cus_cached() {
 }  // namespace
 
 int fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap, int* nw,
-                  int* bc, float* est_us, int* pick) {
+                  int* bc, int* split, float* est_us, int* pick) {
   const Cand* cs = nullptr;
   const int n = candidates(d, &cs);
   if (!n) return 0;
@@ -245,10 +255,11 @@ int fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, in
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
-    const double t = estimate_us(s, cs[i], occupancy(d, causal != 0, i, abs(cs[i].nw)), cus);
+    const double t = estimate_us(s, cs[i], occupancy(d, causal != 0, i, cs[i].nw), cus);
     if (i < cap) {
       if (nw) nw[i] = cs[i].nw;
       if (bc) bc[i] = cs[i].bc;
+      if (split) split[i] = cs[i].split;
       if (est_us) est_us[i] = (float)t;
     }
     if (i == 0 || t < best_t) {
@@ -265,13 +276,16 @@ bool fwd_tile_override_ok(int d) {
   const Cand* cs = nullptr;
   const int n = candidates(d, &cs);
   for (int i = 0; i < n; ++i)
-    if (cs[i].nw == t_override_nw && cs[i].bc == t_override_bc) return true;
+    if (cs[i].nw == t_override_nw && cs[i].bc == t_override_bc &&
+        cs[i].split == t_override_split)
+      return true;
   return false;
 }
 
-void fwd_tile_set_override(int nw, int bc) {
+void fwd_tile_set_override(int nw, int bc, int split) {
   t_override_nw = nw;
   t_override_bc = bc;
+  t_override_split = split;
 }
 
 int fwd_pick_candidate(const FwdArgs& a) {
@@ -279,7 +293,9 @@ int fwd_pick_candidate(const FwdArgs& a) {
   const int n = candidates(a.d, &cs);
   if (t_override_nw) {
     for (int i = 0; i < n; ++i)
-      if (cs[i].nw == t_override_nw && cs[i].bc == t_override_bc) return i;
+      if (cs[i].nw == t_override_nw && cs[i].bc == t_override_bc &&
+          cs[i].split == t_override_split)
+        return i;
   }
   static std::mutex mu;
   static std::unordered_map<std::vector<int>, int, KeyHash> cache;
@@ -293,7 +309,7 @@ int fwd_pick_candidate(const FwdArgs& a) {
   }
   int pick = 0;
   fwd_tile_plan(a.d, a.causal, a.B, a.Hq, a.Hkv, a.Sq, a.Skv, 0, nullptr, nullptr, nullptr,
-                &pick);
+                nullptr, &pick);
   std::lock_guard<std::mutex> lock(mu);
   if (cache.size() > 4096) cache.clear();
   cache[key] = pick;

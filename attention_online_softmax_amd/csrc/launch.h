@@ -86,9 +86,9 @@ hipError_t launch_fwd(const FwdArgs& a);
 // per-candidate estimates; a per-thread override for sweeps and tests.
 int fwd_pick_candidate(const FwdArgs& a);
 int fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap, int* nw,
-                  int* bc, float* est_us, int* pick);
+                  int* bc, int* split, float* est_us, int* pick);
 bool fwd_tile_override_ok(int d);
-void fwd_tile_set_override(int nw, int bc);
+void fwd_tile_set_override(int nw, int bc, int split);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_bwd_d256(const BwdArgs& a);   // d = 256 (bwd256.hip)

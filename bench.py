@@ -816,7 +816,7 @@ def bench_tile_selection(args, hev, stream, reps=10):
         pick, cands = aos.attn_fwd_tile_plan(d, causal, B, Hq, Hkv, S, S)
         n_reps = reps if S < 16384 else max(3, reps // 3)
         for c in cands:
-            aos.attn_fwd_tile_override(c["nw"], c["bc"])
+            aos.attn_fwd_tile_override(c["nw"], c["bc"], c["split"])
 
             def fwd(i):
                 aos.attn_fwd(x["q"], x["k"], x["v"], causal=causal, scale=d ** -0.5, o=o, lse=lse)
@@ -833,8 +833,9 @@ def bench_tile_selection(args, hev, stream, reps=10):
         fastest = min(range(len(cands)), key=lambda i: cands[i]["measured_us"])
         rows.append({"shape": f"B{B} Hq{Hq} Hkv{Hkv} S{S} d{d} {'causal' if causal else 'full'}",
                      "role": role,
-                     "candidates": cands, "pick": [cands[pick]["nw"], cands[pick]["bc"]],
-                     "fastest": [cands[fastest]["nw"], cands[fastest]["bc"]],
+                     "candidates": cands,
+                     "pick": [cands[pick][k] for k in ("nw", "bc", "split")],
+                     "fastest": [cands[fastest][k] for k in ("nw", "bc", "split")],
                      "pick_over_fastest": cands[pick]["measured_us"] / cands[fastest]["measured_us"]})
         print(f"[bench] tiles {rows[-1]['shape']}: pick {rows[-1]['pick']} "
               f"{rows[-1]['pick_over_fastest']:.3f}x fastest {rows[-1]['fastest']}",

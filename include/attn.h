@@ -283,35 +283,37 @@ attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* 
  * Tile selection of the bf16 forward ("Tang, a compiler that derives GPU
  * kernels and bounds how fast they can run", Abstract: a per-tile traffic
  * and time estimate picks the tile).  Calls without a window or bias choose,
- * per shape, among compiled candidates of (waves per workgroup nw, each 32
- * query rows; keys per LDS tile bc): d64 (4,64) (4,32) (8,64) (2,64); d128
- * (4,32) (4,64) (8,32) (8,64); d256 (8,32) (4,32).  d64 and d128 also have
- * key-split candidates, reported with a negative nw: (-4,32) and (-2,32) are
- * |nw| waves on ONE 32-row query block, each taking every |nw|-th 32-key
- * tile with its own softmax state, the states merged at the end by the
- * online-softmax monoid (the same page, Abstract).  They
- * apply only where the grid has at most one 32-row query block per compute
- * unit.  Each candidate's time is estimated from its per-tile matrix-core,
+ * per shape, among compiled candidates (nw, bc, split): nw waves per
+ * workgroup in `split` key groups of nw / split waves each, 32 nw / split
+ * query rows per workgroup; key group g takes the bc-key tiles g,
+ * g + split, g + 2 split, ... with its own softmax state, and the groups'
+ * states of every row are merged at the end by the online-softmax monoid
+ * (the same page, Abstract).  d64: (4,64,1) (4,32,1) (8,64,1) (2,64,1)
+ * (4,32,4) (2,32,2) (4,64,2); d128: (4,32,1) (4,64,1) (8,32,1) (8,64,1)
+ * (4,32,4) (2,32,2) (4,32,2); d256: (8,32,1) (4,32,1).  split = nw (one
+ * 32-row block, every wave its own tiles) applies only where the grid has
+ * at most one 32-row query block per compute unit.  Each candidate's time
+ * is estimated from its per-tile matrix-core,
  * vector and synchronisation cycles, its occupancy on the device and a list
  * schedule of its workgroups; the fastest estimate wins, and the choice is
  * cached per (device, d, causal, B, Hq, Hkv, Sq, Skv).
  *
  * attn_fwd_tile_plan: the candidates for head dim d and the shape, up to cap
- *   of them written to nw[i], bc[i] and est_us[i] (estimated microseconds,
+ *   of them written to nw[i], bc[i], split[i] and est_us[i] (estimated microseconds,
  *   +infinity for a candidate that does not apply to the shape; any array
  *   may be NULL), the index of the one a call would take to *pick.  Returns
  *   the number of candidates, 0 for an unsupported d or an invalid shape.
  *   Needs a current HIP device (occupancy query).
- * attn_fwd_tile_override: for the calling host thread, force (nw, bc) on
- *   later bf16 attn_fwd calls without window or bias (for sweeps and tests),
- *   whether or not the estimate would apply it; (0, 0) returns to the
- *   estimate.  ATTN_ERR_VALUE if exactly one of them is 0 or bc is negative;
- *   a pair not compiled for a later call's d makes that call return
- *   ATTN_ERR_UNSUPPORTED.
+ * attn_fwd_tile_override: for the calling host thread, force (nw, bc, split)
+ *   on later bf16 attn_fwd calls without window or bias (for sweeps and
+ *   tests), whether or not the estimate would apply it; (0, 0, 0) returns to
+ *   the estimate.  ATTN_ERR_VALUE unless all three are 0 or all positive
+ *   with split dividing nw; a triple not compiled for a later call's d makes
+ *   that call return ATTN_ERR_UNSUPPORTED.
  */
 int attn_fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Skv, int cap,
-                       int* nw, int* bc, float* est_us, int* pick);
-attn_status attn_fwd_tile_override(int nw, int bc);
+                       int* nw, int* bc, int* split, float* est_us, int* pick);
+attn_status attn_fwd_tile_override(int nw, int bc, int split);
 
 /*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert aos.attn_abi_version() == 2
+    assert aos.attn_abi_version() == 3
     for s in range(9):
         assert aos.attn_status_str(s) and aos.attn_status_str(s) != "unknown status"
     assert aos.attn_status_str(99) == "unknown status"
@@ -175,17 +175,19 @@ def test_decode_noalloc_validation():
 
 
 def test_fwd_tile_entry_points():
-    """Tile override: exactly one of (nw, bc) zero, or a negative bc, is
-    rejected (a negative nw names a key-split candidate); plan: unsupported
-    head dims and invalid shapes list nothing (both checks happen before any
-    device query)."""
+    """Tile override: all of (nw, bc, split) zero, or all positive with
+    split dividing nw; plan: unsupported head dims and invalid shapes list
+    nothing (both checks happen before any device query)."""
     L = aos.lib()
-    assert L.attn_fwd_tile_override(4, 0) == VALUE
-    assert L.attn_fwd_tile_override(0, 32) == VALUE
-    assert L.attn_fwd_tile_override(-4, -32) == VALUE
-    assert L.attn_fwd_tile_override(4, -32) == VALUE
-    assert L.attn_fwd_tile_override(-4, 32) == 0
-    assert L.attn_fwd_tile_override(0, 0) == 0
+    assert L.attn_fwd_tile_override(4, 0, 1) == VALUE
+    assert L.attn_fwd_tile_override(0, 32, 1) == VALUE
+    assert L.attn_fwd_tile_override(4, 32, 0) == VALUE
+    assert L.attn_fwd_tile_override(-4, 32, 1) == VALUE
+    assert L.attn_fwd_tile_override(4, -32, 1) == VALUE
+    assert L.attn_fwd_tile_override(4, 32, 3) == VALUE      # 3 key groups of 4 waves
+    assert L.attn_fwd_tile_override(4, 32, 4) == 0
+    assert L.attn_fwd_tile_override(4, 64, 2) == 0
+    assert L.attn_fwd_tile_override(0, 0, 0) == 0
     assert aos.attn_fwd_tile_plan(80, True, 1, 1, 1, 64, 64) == (None, [])
     assert aos.attn_fwd_tile_plan(128, True, 1, 3, 2, 64, 64) == (None, [])
     assert aos.attn_fwd_tile_plan(128, True, 1, 2, 2, 65, 64) == (None, [])

@@ -159,22 +159,24 @@ def test_fwd_hidden(case):
 
 
 # The bf16 forward's tiles forced one by one on every kind: the key-split
-# kernel (|nw| waves sharing one 32-row block and splitting its keys, states
-# merged at the end) and a plain tile.  The estimate picks between them by
-# grid size, so neither family's hidden-semantics coverage is left to it.
-FWD_TILES = [(d, causal, kind, nw, bc) for d in (64, 128) for causal in (True, False)
-             for kind in KINDS for nw, bc in ((-4, 32), (-2, 32), (4, 32))]
+# kernel (every wave of a workgroup on one 32-row block, each with its own
+# keys), two key groups sharing their query blocks, and a plain tile; the
+# groups' states are merged at the end.  The estimate picks among them by
+# grid size, so no family's hidden-semantics coverage is left to it.
+FWD_TILES = [(d, causal, kind, nw, bc, sp) for d in (64, 128) for causal in (True, False)
+             for kind in KINDS
+             for nw, bc, sp in ((4, 32, 4), (2, 32, 2), (4, 32, 1), (4, 64 if d == 64 else 32, 2))]
 
 
 @pytest.mark.parametrize("case", FWD_TILES, ids=ids)
 def test_fwd_hidden_forced_tile(case):
-    d, causal, kind, nw, bc = case
+    d, causal, kind, nw, bc, sp = case
     B, Hq, Hkv, Sq, Skv = 1, 2, 1, 300, 333
     cpu, scale = hostile(kind, B, Hq, Hkv, Sq, Skv, d, "bf16", 7300 + d + 2 * causal)
     ref = {k: to_f64(v) for k, v in cpu.items()}
     dev = {k: v.cuda() for k, v in cpu.items()}
     note(f"fwd hidden forced tile {case}")
-    aos.attn_fwd_tile_override(nw, bc)
+    aos.attn_fwd_tile_override(nw, bc, sp)
     try:
         o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
         torch.cuda.synchronize()

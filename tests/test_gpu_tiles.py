@@ -15,9 +15,9 @@ from tests.gpu_util import TOL_LSE, TOL_O, assert_close, inputs, note
 
 pytestmark = pytest.mark.gpu
 
-CANDS = {64: [(4, 64), (4, 32), (8, 64), (2, 64), (-4, 32), (-2, 32)],
-         128: [(4, 32), (4, 64), (8, 32), (8, 64), (-4, 32), (-2, 32)],
-         256: [(8, 32), (4, 32)]}
+CANDS = {64: [(4, 64, 1), (4, 32, 1), (8, 64, 1), (2, 64, 1), (4, 32, 4), (2, 32, 2), (4, 64, 2)],
+         128: [(4, 32, 1), (4, 64, 1), (8, 32, 1), (8, 64, 1), (4, 32, 4), (2, 32, 2), (4, 32, 2)],
+         256: [(8, 32, 1), (4, 32, 1)]}
 # (B, Hq, Hkv, Sq, Skv, causal): ragged tails, grouped heads, Sq < Skv.
 SHAPES = [(1, 4, 2, 300, 300, True), (2, 2, 1, 77, 333, False), (1, 2, 2, 200, 460, True)]
 
@@ -25,12 +25,13 @@ SHAPES = [(1, 4, 2, 300, 300, True), (2, 2, 1, 77, 333, False), (1, 2, 2, 200, 4
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_plan_lists_the_compiled_candidates(d):
     pick, cands = aos.attn_fwd_tile_plan(d, True, 4, 16, 16, 2048, 2048)
-    assert [(c["nw"], c["bc"]) for c in cands] == CANDS[d]
+    assert [(c["nw"], c["bc"], c["split"]) for c in cands] == CANDS[d]
     assert 0 <= pick < len(cands)
-    # The key-split candidates apply only to grids of at most one 32-row
-    # query block per compute unit; every plain candidate has an estimate.
+    # The key-split candidates (one 32-row block, split = nw) apply only to
+    # grids of at most one such block per compute unit; every other
+    # candidate has an estimate.
     for c in cands:
-        if c["nw"] > 0:
+        if c["split"] < c["nw"]:
             assert c["est_us"] > 0 and math.isfinite(c["est_us"])
         else:
             assert c["est_us"] is None
@@ -43,7 +44,7 @@ def test_plan_key_split_on_a_tiny_grid(d):
     # 8 query blocks x 8 heads: 64 workgroups of the key-split kernel, far
     # fewer than compute units; it gets an estimate there.
     pick, cands = aos.attn_fwd_tile_plan(d, False, 1, 8, 8, 256, 256)
-    ks = [c for c in cands if c["nw"] < 0]
+    ks = [c for c in cands if c["split"] == c["nw"]]
     assert ks and all(c["est_us"] is not None and c["est_us"] > 0 for c in ks)
 
 
@@ -55,21 +56,21 @@ def test_every_candidate_parity(d, shape):
     dev, ref = inputs(B, Hq, Hkv, Sq, Skv, d, "bf16", 600 + d + Sq)
     scale = 1 / math.sqrt(d)
     O, L = oracle.attention_ref(ref["q"], ref["k"], ref["v"], causal, scale)
-    for nw, bc in CANDS[d]:
-        note(f"tile candidate nw{nw} bc{bc} d{d} {shape}")
-        aos.attn_fwd_tile_override(nw, bc)
+    for nw, bc, sp in CANDS[d]:
+        note(f"tile candidate nw{nw} bc{bc} split{sp} d{d} {shape}")
+        aos.attn_fwd_tile_override(nw, bc, sp)
         try:
             o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
             torch.cuda.synchronize()
         finally:
             aos.attn_fwd_tile_override(0, 0)
-        assert_close(to_f64(o), O, TOL_O["bf16"], f"nw{nw} bc{bc} O")
-        assert_close(lse.cpu().numpy(), L, TOL_LSE["bf16"], f"nw{nw} bc{bc} LSE")
+        assert_close(to_f64(o), O, TOL_O["bf16"], f"nw{nw} bc{bc} split{sp} O")
+        assert_close(lse.cpu().numpy(), L, TOL_LSE["bf16"], f"nw{nw} bc{bc} split{sp} LSE")
 
 
 def test_override_not_compiled_is_rejected():
     dev, _ = inputs(1, 2, 2, 64, 64, 256, "bf16", 5)
-    aos.attn_fwd_tile_override(2, 64)   # not a d256 candidate
+    aos.attn_fwd_tile_override(2, 64, 1)   # not a d256 candidate
     try:
         with pytest.raises(aos.AttnError):
             aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
