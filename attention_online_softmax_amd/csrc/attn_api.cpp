@@ -81,9 +81,9 @@ thread_local int g_n_events = 0;
 }  // namespace
 
 namespace attn {
-void timing_mark(hipStream_t stream, int slot) {
-  if (g_events && slot < g_n_events && g_events[slot])
-    (void)hipEventRecord((hipEvent_t)g_events[slot], stream);
+void timing_events(int i, hipEvent_t* start, hipEvent_t* stop) {
+  *start = (g_events && 2 * i < g_n_events) ? (hipEvent_t)g_events[2 * i] : nullptr;
+  *stop = (g_events && 2 * i + 1 < g_n_events) ? (hipEvent_t)g_events[2 * i + 1] : nullptr;
 }
 }  // namespace attn
 

@@ -28,11 +28,11 @@ static hipError_t launch_dkdv_fused_t(const BwdArgs& a, float* dqacc) {
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(n_ktiles * BHk),
-                     dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, 0,
-                     nullptr, 0, 0, a.scale, a.scale * kLog2e, rows_pad, a.Skv - a.Sq, dqacc);
+  ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(n_ktiles * BHk),
+              dim3(256), a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+              (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
+              (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, 0,
+              nullptr, 0, 0, a.scale, a.scale * kLog2e, rows_pad, a.Skv - a.Sq, dqacc);
   return hipGetLastError();
 }
 

@@ -78,23 +78,17 @@ static hipError_t launch_bwd_fused_t(const BwdArgs& a) {
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
   float* dqacc = a.ws + bwd_fused_acc_offset(a.B, a.Hq, a.Sq);
   const int64_t n4 = (int64_t)a.B * a.Hq * a.Sq * D / 4;   // float4 of the accumulator
-  timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows_pad + 127) / 128)), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, dqacc,
-                     n4, rows_pad, a.Sq, Sqp);
-  timing_mark(a.stream, 1);
+  ATTN_LAUNCH(0, (bwd_prep_kernel<D>), dim3((unsigned)((rows_pad + 127) / 128)), dim3(256),
+              a.stream, (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.ws, dqacc,
+              n4, rows_pad, a.Sq, Sqp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_mark(a.stream, 2);
-  e = launch_dkdv_fused(a, dqacc);
-  timing_mark(a.stream, 3);
+  e = launch_dkdv_fused(a, dqacc);   // kernel 1 of the call
   if (e != hipSuccess) return e;
   // A grid of 8 workgroups per compute unit, four elements per thread and step.
   const int64_t cgrid = std::min<int64_t>((n4 + 255) / 256, 2048);
-  timing_mark(a.stream, 4);
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)cgrid), dim3(256), 0, a.stream,
-                     (const float*)dqacc, (uint16_t*)a.dq, n4, a.scale);
-  timing_mark(a.stream, 5);
+  ATTN_LAUNCH(2, bwd_dq_convert_kernel, dim3((unsigned)cgrid), dim3(256), a.stream,
+              (const float*)dqacc, (uint16_t*)a.dq, n4, a.scale);
   return hipGetLastError();
 }
 

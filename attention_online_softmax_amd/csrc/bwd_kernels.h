@@ -542,31 +542,27 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   // dQ first: it also writes the (D, nl) pairs the dK/dV kernel reads.
   const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
-  timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_qtiles * BH), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
-                     BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
-                     a.scale, sl2, n_qtiles);
-  timing_mark(a.stream, 1);
+  ATTN_LAUNCH(0, (bwd_dq_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_qtiles * BH), dim3(256), a.stream,
+              (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+              (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
+              BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
+              a.scale, sl2, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
-  timing_mark(a.stream, 2);
   // At d = 256 a call without the causal mask runs the causal dK/dV kernel
   // with the diagonal past the last key (i + Skv >= every key j for every
   // query i), which masks nothing: the non-causal instantiation does not
   // fit the registers of that head dimension and spills.
   constexpr bool AS_CAUSAL = CAUSAL || (D >= 256 && !WIN);
   const int diag = CAUSAL ? a.Skv - a.Sq : a.Skv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false>), dim3(n_ktiles * BHk),
-                     dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv,
-                     a.window, a.bias, a.bias_sb, a.bias_sh, a.scale, sl2, rows_pad, diag,
-                     nullptr);
-  timing_mark(a.stream, 3);
+  ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false>), dim3(n_ktiles * BHk),
+              dim3(256), a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+              (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
+              (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv,
+              a.window, a.bias, a.bias_sb, a.bias_sh, a.scale, sl2, rows_pad, diag,
+              nullptr);
   return hipGetLastError();
 }
 

@@ -735,18 +735,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int chunk = (a.Skv + a.n_splits - 1) / a.n_splits;
   const int n_items = a.n_splits * a.Hkv * n_hchunks * a.B;
   const int grid = n_items < device_cus() ? n_items : device_cus();
-  timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3(grid), dim3(kDecodeThreads), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.ws, a.B, a.Hq,
-                     a.Hkv, a.Skv, chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
-  timing_mark(a.stream, 1);
+  ATTN_LAUNCH(0, (decode_split_kernel<T, D, GC>), dim3(grid), dim3(kDecodeThreads),
+              a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.ws, a.B, a.Hq,
+              a.Hkv, a.Skv, chunk, a.n_splits, n_hchunks, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BHq = a.B * a.Hq;
-  timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((BHq + 3) / 4), dim3(256), 0, a.stream,
-                     (const float*)a.ws, (T*)a.o, a.lse, BHq, a.n_splits);
-  timing_mark(a.stream, 3);
+  ATTN_LAUNCH(1, (decode_combine_kernel<T, D>), dim3((BHq + 3) / 4), dim3(256), a.stream,
+              (const float*)a.ws, (T*)a.o, a.lse, BHq, a.n_splits);
   return hipGetLastError();
 }
 
@@ -771,24 +767,20 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a) {
   // One workgroup (four waves) per compute unit, each wave a stream of units.
   const int wgs = (n_units + 3) / 4;
   const int grid = wgs < device_cus() ? wgs : device_cus();
-  timing_mark(a.stream, 0);
   if (a.pg.table)
-    hipLaunchKernelGGL((decode_split_mfma_kernel<D, true>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
-                       a.B, a.Hq, a.Hkv, 0, a.n_splits, n_hchunks, a.scale * kLog2e, a.pg);
+    ATTN_LAUNCH(0, (decode_split_mfma_kernel<D, true>), dim3(grid), dim3(256), a.stream,
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
+                a.B, a.Hq, a.Hkv, 0, a.n_splits, n_hchunks, a.scale * kLog2e, a.pg);
   else
-    hipLaunchKernelGGL((decode_split_mfma_kernel<D, false>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
-                       a.B, a.Hq, a.Hkv, a.Skv, a.n_splits, n_hchunks, a.scale * kLog2e,
-                       PagedKV{nullptr, nullptr, 0, 0, 0});
-  timing_mark(a.stream, 1);
+    ATTN_LAUNCH(0, (decode_split_mfma_kernel<D, false>), dim3(grid), dim3(256), a.stream,
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ws,
+                a.B, a.Hq, a.Hkv, a.Skv, a.n_splits, n_hchunks, a.scale * kLog2e,
+                PagedKV{nullptr, nullptr, 0, 0, 0});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BHq = a.B * a.Hq;
-  timing_mark(a.stream, 2);
-  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3((BHq + 3) / 4), dim3(256), 0,
-                     a.stream, (const float*)a.ws, (uint16_t*)a.o, a.lse, BHq, a.n_splits);
-  timing_mark(a.stream, 3);
+  ATTN_LAUNCH(1, (decode_combine_kernel<uint16_t, D>), dim3((BHq + 3) / 4), dim3(256),
+              a.stream, (const float*)a.ws, (uint16_t*)a.o, a.lse, BHq, a.n_splits);
   return hipGetLastError();
 }
 

@@ -828,13 +828,10 @@ static hipError_t launch_fwd_f32_k(const FwdArgs& a) {
   constexpr int ROWS = NT / KW / TPR;
   const int n_qtiles = (a.Sq + ROWS - 1) / ROWS;
   const int BH = a.B * a.Hq;
-  timing_mark(a.stream, 0);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TPR, NT, KW, BIAS>), dim3(n_qtiles * BH), dim3(NT),
-                     0, a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
-                     a.scale * kLog2e, n_qtiles);
-  timing_mark(a.stream, 1);
+  ATTN_LAUNCH(0, (fwd_f32_kernel<D, CAUSAL, TPR, NT, KW, BIAS>), dim3(n_qtiles * BH), dim3(NT),
+              a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
+              a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
+              a.scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 
@@ -867,16 +864,14 @@ static hipError_t launch_fwd_bf16_k(const FwdArgs& a) {
   constexpr int BR = 32 * NW / SPLIT;   // query rows per workgroup
   const int n_qtiles = (a.Sq + BR - 1) / BR;
   const int BH = a.B * a.Hq;
-  timing_mark(a.stream, 0);
   // Items of (query tile, batch, key/value head) in groups of 8, one
   // workgroup per query head of each (see the kernel's work mapping).
   const int items = n_qtiles * a.B * a.Hkv;
   const int grid = (items + 7) / 8 * 8 * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, WIN, BIAS, SPLIT>), dim3(grid),
-                     dim3(64 * NW), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
-                     a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
-  timing_mark(a.stream, 1);
+  ATTN_LAUNCH(0, (fwd_bf16_kernel<D, CAUSAL, NW, BC, WIN, BIAS, SPLIT>), dim3(grid),
+              dim3(64 * NW), a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+              (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.Hq, a.Hkv, a.Sq, a.Skv,
+              a.window, a.bias, a.bias_sb, a.bias_sh, a.scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 
@@ -901,12 +896,10 @@ static hipError_t fwd_candidate_ks(const FwdArgs* a, const void** fn) {
   const int n_qtiles = (a->Sq + 31) / 32;
   const int items = n_qtiles * a->B * a->Hkv;
   const int grid = (items + 7) / 8 * 8 * (a->Hq / a->Hkv);
-  timing_mark(a->stream, 0);
-  hipLaunchKernelGGL((fwd_bf16_ks_kernel<D, CAUSAL, NW>), dim3(grid), dim3(64 * NW), 0, a->stream,
-                     (const uint16_t*)a->q, (const uint16_t*)a->k, (const uint16_t*)a->v,
-                     (uint16_t*)a->o, a->lse, a->B * a->Hq, a->Hq, a->Hkv, a->Sq, a->Skv,
-                     a->scale * kLog2e, n_qtiles);
-  timing_mark(a->stream, 1);
+  ATTN_LAUNCH(0, (fwd_bf16_ks_kernel<D, CAUSAL, NW>), dim3(grid), dim3(64 * NW), a->stream,
+              (const uint16_t*)a->q, (const uint16_t*)a->k, (const uint16_t*)a->v,
+              (uint16_t*)a->o, a->lse, a->B * a->Hq, a->Hq, a->Hkv, a->Sq, a->Skv,
+              a->scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 

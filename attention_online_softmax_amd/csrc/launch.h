@@ -2,6 +2,7 @@
 // launchers.  Arguments are validated before any of these is filled in.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -76,9 +77,9 @@ inline int device_cus() {
   return cus;
 }
 
-// Records the caller's timing event for `slot` (2i before / 2i+1 after the
-// i-th kernel of the current entry point) if timing events are set.
-void timing_mark(hipStream_t stream, int slot);
+// The caller's timing events for the i-th kernel of the current entry point
+// (slots 2i and 2i + 1; null where none is set).
+void timing_events(int i, hipEvent_t* start, hipEvent_t* stop);
 
 hipError_t launch_fwd(const FwdArgs& a);
 // bf16 forward tile selection (fwd_tiles.cpp): index of the compiled
@@ -100,3 +101,18 @@ int64_t bwd_fused_acc_offset(int B, int Hq, int Sq);
 hipError_t launch_dkdv_fused(const BwdArgs& a, float* dqacc);
 
 }  // namespace attn
+
+// Launch of the i-th kernel of an entry point.  While the caller has timing
+// events set for it, they are bound to the launch itself (hipExtLaunchKernel
+// records the kernel's start and end in them), so timing adds no packet of
+// its own to the stream and no gap between kernels.
+#define ATTN_LAUNCH(i, kernel, grid, block, stream, ...)                                \
+  do {                                                                                  \
+    hipEvent_t attn_e0_ = nullptr, attn_e1_ = nullptr;                                  \
+    ::attn::timing_events((i), &attn_e0_, &attn_e1_);                                   \
+    if (attn_e0_ || attn_e1_)                                                           \
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, attn_e0_, attn_e1_, 0,      \
+                            __VA_ARGS__);                                               \
+    else                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                  \
+  } while (0)

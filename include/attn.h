@@ -318,9 +318,10 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split);
 /*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles
  * created by the caller.  While set (per calling host thread), every entry
- * point records events[2i] on its stream just before the i-th kernel it
- * launches and events[2i+1] just after it, for 2i+1 < n; the caller reads
- * the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
+ * point binds events[2i] and events[2i+1] (those with index < n) to the i-th
+ * kernel it launches, through hipExtLaunchKernel: they record that kernel's
+ * start and end on its stream, with no packet of their own between kernels;
+ * the caller reads the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
  * (the forward kernel), attn_decode and attn_decode_paged 2 (split,
  * combine), attn_bwd 2
  * (dQ together with D = rowsum(dO*O), then dK/dV), attn_bwd_fused 3.  Pass NULL or n = 0 to stop.  The library
