@@ -318,10 +318,11 @@ def quantiles(xs):
 
 
 def run_calls(calls, n_kernels, hev, steps, stream, slots=None):
-    """Run `steps` iterations of the ABI calls with HIP events recorded by the
-    library around kernels.  slots: {call: set of event slots to record}
-    (slot 2i = before kernel i, 2i+1 = after it); None records every slot.
-    Slots left out get no event, so no marker lands between those kernels.
+    """Run `steps` iterations of the ABI calls with HIP events bound by the
+    library to its kernel launches.  slots: {call: set of event slots to
+    record} (slot 2i = start of kernel i, 2i+1 = its end); None records every
+    slot.  The events ride on the launches themselves, so none of them adds a
+    packet or a gap to the stream.
     Returns (total ms between events bracketing all steps,
     {call: [[ms of kernel i, or None] per step]},
     {call: [ms from first recorded slot to last recorded slot] per step})."""
