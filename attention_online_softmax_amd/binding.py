@@ -26,7 +26,7 @@ EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
            "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_fused_workspace_bytes",
            "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc",
-           "attn_fwd_tile_plan", "attn_fwd_tile_override")
+           "attn_fwd_tile_plan", "attn_fwd_tile_override", "attn_bwd_tile_override")
 SCRATCH_BYTES = 8 << 20   # ATTN_SCRATCH_BYTES of attn.h
 
 _lib = None
@@ -81,6 +81,8 @@ def lib():
     L.attn_fwd_tile_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, ip, fp, ip]
     L.attn_fwd_tile_override.restype = i
     L.attn_fwd_tile_override.argtypes = [i, i, i]
+    L.attn_bwd_tile_override.restype = i
+    L.attn_bwd_tile_override.argtypes = [i, i]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -138,6 +140,15 @@ def attn_fwd_tile_override(nw=0, bc=0, split=1):
     st = lib().attn_fwd_tile_override(int(nw), int(bc), int(split))
     if st:
         raise AttnError(st, "attn_fwd_tile_override")
+
+
+def attn_bwd_tile_override(nkw=0, hs=0):
+    """Force the dK/dV launch shape (32-key blocks per workgroup, wave
+    groups) on this thread's later backward calls at d <= 128: (4, 1),
+    (4, 2) or (2, 4); (0, 0) returns to the library's choice."""
+    st = lib().attn_bwd_tile_override(int(nkw), int(hs))
+    if st:
+        raise AttnError(st, "attn_bwd_tile_override")
 
 
 def attn_decode_workspace_bytes(B, Hq, d, n_splits):

@@ -7,6 +7,8 @@
 #include "../../include/attn.h"
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include <mutex>
@@ -81,6 +83,60 @@ thread_local int g_n_events = 0;
 }  // namespace
 
 namespace attn {
+static thread_local int t_dkdv_nkw = 0, t_dkdv_hs = 0;
+void bwd_set_dkdv_override(int nkw, int hs) {
+  t_dkdv_nkw = nkw;
+  t_dkdv_hs = hs;
+}
+void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
+  if (t_dkdv_nkw) {
+    *nkw = t_dkdv_nkw;
+    *hs = t_dkdv_hs;
+    return;
+  }
+  // Estimated time of each shape, in units of one wave's pass over one
+  // query iteration (query head, 32-row query tile) of its 32-key block:
+  // the larger of the grid's load per compute unit and the longest
+  // workgroup.  Per 128 keys the iterations are the query tiles that can
+  // see those keys (causal and window bounds, as in the kernel) times the
+  // G query heads of the key/value head.  The load is their sum over the
+  // 128-key workgroups divided by the compute units (two waves share each
+  // SIMD in every shape).  The longest workgroup, n_max iterations: about
+  // 1.3 n_max for the plain kernel (its heavy workgroups end up alone on a
+  // compute unit, one wave per SIMD), n_max for (4, 2) (two groups, two
+  // waves per SIMD), n_max / 2 for (2, 4).  The grouped shapes pay for the
+  // merge and, with 64 keys per workgroup, for loading every Q / dO tile
+  // twice as often: 5 % for (4, 2); for (2, 4) 5 % with grouped heads and
+  // 40 % without (measured on MI355X: short iteration lists amortise the
+  // per-workgroup costs worst).  Ties go to the plain kernel.
+  const int G = a.Hq / a.Hkv;
+  const int off = a.causal ? a.Skv - a.Sq : a.Skv;
+  const bool win = a.causal && a.window > 0;
+  const int nk = (a.Skv + 127) / 128;
+  double sum = 0.0;
+  int nq_max = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int q_start = a.causal ? (std::max(0, kt * 128 - off) / 32) * 32 : 0;
+    const int q_end = win ? std::min(a.Sq, kt * 128 + 127 - off + a.window) : a.Sq;
+    const int nq = std::max(0, (q_end - q_start + 31) / 32);
+    sum += nq;
+    nq_max = std::max(nq_max, nq);
+  }
+  const double load = sum * a.B * a.Hkv * G / device_cus();
+  const double n_max = (double)nq_max * G;
+  const double t41 = std::max(load, 1.3 * n_max);
+  const double t42 = std::max(1.05 * load, n_max);
+  const double t24 = std::max((G > 1 ? 1.05 : 1.40) * load, 0.5 * n_max);
+  *nkw = 4;
+  *hs = 1;
+  if (t42 < t41 && t42 <= t24) {
+    *hs = 2;
+  } else if (t24 < t41 && t24 < t42) {
+    *nkw = 2;
+    *hs = 4;
+  }
+}
+
 void timing_events(int i, hipEvent_t* start, hipEvent_t* stop) {
   *start = (g_events && 2 * i < g_n_events) ? (hipEvent_t)g_events[2 * i] : nullptr;
   *stop = (g_events && 2 * i + 1 < g_n_events) ? (hipEvent_t)g_events[2 * i + 1] : nullptr;
@@ -112,6 +168,14 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split) {
   const bool none = nw == 0 && bc == 0 && split == 0;
   if (!none && (nw <= 0 || bc <= 0 || split <= 0 || nw % split != 0)) return ATTN_ERR_VALUE;
   attn::fwd_tile_set_override(nw, bc, split);
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_tile_override(int nkw, int hs) {
+  const bool ok = (nkw == 0 && hs == 0) || (nkw == 4 && hs == 1) || (nkw == 4 && hs == 2) ||
+                  (nkw == 2 && hs == 4);
+  if (!ok) return ATTN_ERR_VALUE;
+  attn::bwd_set_dkdv_override(nkw, hs);
   return ATTN_OK;
 }
 

@@ -73,13 +73,25 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
 template <int D>
 constexpr int kBwdMinWaves = D >= 256 ? 1 : 2;
 
-template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED>
-__global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
+// Small grids (fewer 128-key workgroups than compute units, e.g. grouped
+// heads with few key/value heads): NKW 32-key blocks per workgroup and HS
+// groups of NKW waves.  Group h takes every HS-th iteration (query head,
+// query tile) of the loop, h, h + HS, ..., with Q/dO slots of its own, and at
+// the end groups 1 .. HS-1 add their dK/dV sums into group 0's through LDS.
+// (NKW, HS) = (4, 1) is the plain kernel; (4, 2) and (2, 4) run eight waves,
+// two per SIMD, on the same number of keys or half of them.
+template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED, int NKW = 4, int HS = 1>
+__global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
     const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale, float scale_log2,
     int64_t rows_pad, int diag, float* __restrict__ dqacc) {
+  static_assert((NKW == 4 && HS == 1) || (!FUSED && D <= 128 && NKW * HS == 8 &&
+                                          (HS - 1) * NKW <= 2 * HS),
+                "(4, 1), or eight waves of a plain kernel at d <= 128");
+  constexpr int NW = NKW * HS;   // waves per workgroup
+  constexpr int KT = 32 * NKW;   // keys per workgroup
   constexpr int QT = 32;   // query rows per tile
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
@@ -91,20 +103,22 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
   // dS staging (FUSED): 32 query rows of 128 keys, padded so that both the
   // column writes and the row reads are free of bank conflicts.
   constexpr int SSTR = 128 + 8;
-  __shared__ __attribute__((aligned(1024))) uint16_t sT0[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sT1[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[128 * D];   // K rows when FUSED
+  __shared__ __attribute__((aligned(1024))) uint16_t sT0[HS * SLOT];   // one slot per group
+  __shared__ __attribute__((aligned(1024))) uint16_t sT1[HS * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[KT * D];   // K rows when FUSED
   __shared__ __attribute__((aligned(16))) uint16_t sS[FUSED ? QT * SSTR : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
+  const int kbw = HS == 1 ? wave : wave % NKW;   // the wave's key block, and its index in the group
+  const int hg = HS == 1 ? 0 : wave / NKW;       // its group
   const int n = lane & 31, g = lane >> 5;
   const int bhk = blockIdx.x % BHk;
   const int ktile = blockIdx.x / BHk;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int G = Hq / Hkv;
   const int off = diag;   // key j is visible to query i iff j <= i + off (causal)
-  const int key0_wave = ktile * 128 + wave * 32;
+  const int key0_wave = ktile * KT + kbw * 32;
   // Lane n owns key swap23(n) of the wave's 32: the V rows it needs as the
   // B operand of dP are then read exactly like the Q and dO rows.
   const int key = key0_wave + swap23(n);
@@ -117,8 +131,8 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
   // with a sliding window of `window` keys (causal only, 0 = none) also
   // i < last_key - off + window.
   const bool win = WIN;   // instantiated for causal calls with window > 0 only
-  const int q_start = CAUSAL ? (max(0, ktile * 128 - off) / QT) * QT : 0;
-  const int q_end = win ? min(Sq, ktile * 128 + 127 - off + window) : Sq;
+  const int q_start = CAUSAL ? (max(0, ktile * KT - off) / QT) * QT : 0;
+  const int q_end = win ? min(Sq, ktile * KT + KT - 1 - off + window) : Sq;
   // Query tiles per head; 0 when no query's window reaches these keys
   // (possible only with a window and Sq < Skv).
   const int n_qt = max(0, (q_end - q_start + QT - 1) / QT);
@@ -126,32 +140,49 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
 
   // The workgroup's V rows, K rows when FUSED (rows past Skv arrive as zeros).
   {
-    TileDma<D, 128, 4> vdma;
+    TileDma<D, KT, NW> vdma;
     vdma.init(wave, lane);
-    vdma.load(FUSED ? Kh : Vh, Skv, sV, ktile * 128, wave);
+    vdma.load(FUSED ? Kh : Vh, Skv, sV, ktile * KT, wave);
   }
-  TileDma<D, QT, 4> dma;
-  dma.init(wave, lane);
+  TileDma<D, QT, NKW> dma;   // the group's tiles, moved by its NKW waves
+  dma.init(kbw, lane);
   // The (D, nl) pairs of a tile's 32 rows: 256 contiguous bytes, one float
   // per lane of wave 0, through a descriptor over the whole workspace
   // (< 4 GiB).
   const rsrc_t ws_rs = make_rsrc(ws, (uint32_t)(2 * rows_pad * 4));
-  // Transfer of the next iteration tile (query head dma_hh, query tile
-  // dma_qt) into `slot`; past the last tile nothing is fetched.
+  // Transfer of the group's next iteration tile (query head dma_hh, query
+  // tile dma_qt) into its part of `slot`; past the last tile nothing is
+  // fetched.  Iterations advance by HS: (hh, qt) moves HS tiles on.
+  auto advance = [&](int& hh, int& qt, int by) {
+    qt += by;
+    while (qt >= n_qt && hh < G) {   // at most HS passes (n_qt >= 1 when it matters)
+      qt -= n_qt;
+      ++hh;
+    }
+  };
   int dma_hh = 0, dma_qt = 0;
-  auto issue = [&](uint16_t* slot) {
+  if constexpr (HS > 1) {
+    if (n_qt > 0) advance(dma_hh, dma_qt, hg);
+    else dma_hh = G;
+  }
+  auto issue = [&](uint16_t* slot0) {
     if (dma_hh >= G) return;
+    uint16_t* slot = slot0 + hg * SLOT;
     const int q0 = q_start + dma_qt * QT;
     const int64_t bh = (int64_t)b * Hq + hk * G + dma_hh;
-    if (wave == 0)
+    if (kbw == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ws_rs, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, lane * 4,
           (int)((uint32_t)(bh * Sqp + q0) * 8), 0, 0);
-    dma.load(Q + bh * Sq * D, Sq, slot, q0, wave);
-    dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, wave);
-    if (++dma_qt == n_qt) {
-      dma_qt = 0;
-      ++dma_hh;
+    dma.load(Q + bh * Sq * D, Sq, slot, q0, kbw);
+    dma.load(dO + bh * Sq * D, Sq, slot + QT * D, q0, kbw);
+    if constexpr (HS == 1) {
+      if (++dma_qt == n_qt) {
+        dma_qt = 0;
+        ++dma_hh;
+      }
+    } else {
+      advance(dma_hh, dma_qt, HS);
     }
   };
   issue(sT0);
@@ -172,7 +203,7 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
   int r_off[kRowOffs<D>], t_off[kTrOffs<D>];
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
-  const uint16_t* sVw = sV + wave * 32 * D;
+  const uint16_t* sVw = sV + kbw * 32 * D;
 
   // One tile: S = Q K^T and dP = dO V^T (element i: query 16*(i/8) + 8g +
   // i%8 of the tile, key `key`); P = exp(scale S - LSE), dS = P (dP - D);
@@ -302,18 +333,28 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
     }
   };
 
-  int cur_qt = 0, cur_hh = 0;   // query tile and query head of the next step
-  auto body = [&](const uint16_t* cur, uint16_t* nxt) {
+  int cur_qt = 0, cur_hh = 0;   // query tile and query head of the group's next step
+  if constexpr (HS > 1) {
+    if (n_qt > 0) advance(cur_hh, cur_qt, hg);
+    else cur_hh = G;
+  }
+  auto body = [&](const uint16_t* cur0, uint16_t* nxt) {
     wait_vmcnt0();   // this wave's part of the current tile (and V) has landed
     lds_barrier();   // ... and every wave's; the other slot is no longer read
     opaque_offsets<kRowOffs<D>>(r_off);
     opaque_offsets<kTrOffs<D>>(t_off);
     issue(nxt);
+    const uint16_t* cur = cur0 + hg * SLOT;
     const int qs = q_start + cur_qt * QT;
     const int hh = cur_hh;
-    if (++cur_qt == n_qt) {
-      cur_qt = 0;
-      ++cur_hh;
+    if constexpr (HS == 1) {
+      if (++cur_qt == n_qt) {
+        cur_qt = 0;
+        ++cur_hh;
+      }
+    } else {
+      if (hh >= G) return;   // the group has no iteration left (the last step)
+      advance(cur_hh, cur_qt, HS);
     }
     // Tiles whose queries all precede this wave's first visible key, or
     // whose windows all start after its last key: skip (FUSED: the dQ
@@ -327,12 +368,56 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
       dq_tile(qs, hh);
     }
   };
+  const int n_steps = (n_it + HS - 1) / HS;   // steps of every group (the last may be idle)
 #pragma clang loop unroll(disable)
-  for (int i = 0; i < n_it; i += 2) {
+  for (int i = 0; i < n_steps; i += 2) {
     body(sT0, sT1);
-    if (i + 1 < n_it) body(sT1, sT0);
+    if (i + 1 < n_steps) body(sT1, sT0);
   }
   wait_vmcnt0();   // nothing in flight into LDS when the workgroup ends (n_it may be 0)
+  if constexpr (HS > 1) {
+    // Groups 1 .. HS-1 add their sums into group 0's: one half of the
+    // columns of one accumulator per round, group h's partial of the wave
+    // with key block kb at red[((h - 1) NKW + kb) 32 D / 2 + ...] (floats),
+    // laid out by lane so that writes and reads are plain 16-byte rows.
+    float* red = reinterpret_cast<float*>(sT0);
+    constexpr int HALF = NDB / 2 > 0 ? NDB / 2 : 1;   // accumulator blocks per round
+    constexpr int ROUNDS = NDB / HALF;
+#pragma unroll
+    for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        lds_barrier();   // the slots (and the previous round) are no longer read
+        f32x16* A = acc == 0 ? dvt : dkt;
+        if (hg > 0) {
+          float* dst = red + ((hg - 1) * NKW + kbw) * (HALF * 16 * 64) + lane * 4;
+#pragma unroll
+          for (int e = 0; e < HALF; ++e)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *(f32x4*)(dst + (e * 4 + i4) * 256) =
+                  f32x4{A[rd * HALF + e][4 * i4], A[rd * HALF + e][4 * i4 + 1],
+                        A[rd * HALF + e][4 * i4 + 2], A[rd * HALF + e][4 * i4 + 3]};
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's writes are done
+        lds_barrier();
+        if (hg == 0) {
+#pragma unroll
+          for (int h = 1; h < HS; ++h) {
+            const float* src = red + ((h - 1) * NKW + kbw) * (HALF * 16 * 64) + lane * 4;
+#pragma unroll
+            for (int e = 0; e < HALF; ++e)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 v = *(const f32x4*)(src + (e * 4 + i4) * 256);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) A[rd * HALF + e][4 * i4 + j] += v[j];
+              }
+          }
+        }
+      }
+    if (hg > 0) return;
+  }
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
   store_transposed<NDB>(dK + kro, dkt, g, scale);
@@ -549,7 +634,6 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
               a.scale, sl2, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_ktiles = (a.Skv + 127) / 128;
   const int BHk = a.B * a.Hkv;
   // At d = 256 a call without the causal mask runs the causal dK/dV kernel
   // with the diagonal past the last key (i + Skv >= every key j for every
@@ -557,12 +641,31 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   // fit the registers of that head dimension and spills.
   constexpr bool AS_CAUSAL = CAUSAL || (D >= 256 && !WIN);
   const int diag = CAUSAL ? a.Skv - a.Sq : a.Skv;
-  ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false>), dim3(n_ktiles * BHk),
-              dim3(256), a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-              (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
-              (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv,
-              a.window, a.bias, a.bias_sb, a.bias_sh, a.scale, sl2, rows_pad, diag,
-              nullptr);
+  auto dkdv = [&](auto nkw, auto hs) {
+    constexpr int NKW = decltype(nkw)::value, HS = decltype(hs)::value;
+    const int n_ktiles = (a.Skv + 32 * NKW - 1) / (32 * NKW);
+    ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false, NKW, HS>),
+                dim3(n_ktiles * BHk), dim3(64 * NKW * HS), a.stream, (const uint16_t*)a.q,
+                (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
+                (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq,
+                Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh, a.scale, sl2, rows_pad,
+                diag, nullptr);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  if constexpr (D <= 128) {
+    int nkw, hs;
+    bwd_dkdv_config(a, &nkw, &hs);
+    if (nkw == 2 && hs == 4)
+      dkdv(I2{}, I4{});
+    else if (nkw == 4 && hs == 2)
+      dkdv(I4{}, I2{});
+    else
+      dkdv(I4{}, I1{});
+  } else {
+    dkdv(I4{}, I1{});
+  }
   return hipGetLastError();
 }
 

@@ -92,6 +92,12 @@ bool fwd_tile_override_ok(int d);
 void fwd_tile_set_override(int nw, int bc, int split);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+// dK/dV launch shape of a call at d <= 128: key blocks of 32 per workgroup
+// (nkw) and wave groups that split the query iterations (hs): (4, 1), or
+// (4, 2) / (2, 4) on grids of fewer 128-key workgroups than compute units;
+// and a per-thread override for sweeps and tests ((0, 0) = none).
+void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs);
+void bwd_set_dkdv_override(int nkw, int hs);
 hipError_t launch_bwd_d256(const BwdArgs& a);   // d = 256 (bwd256.hip)
 // Fused variant (no window or bias): ws holds the (D, nl) pairs, then from
 // bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].

@@ -316,6 +316,19 @@ int attn_fwd_tile_plan(int d, int causal, int B, int Hq, int Hkv, int Sq, int Sk
 attn_status attn_fwd_tile_override(int nw, int bc, int split);
 
 /*
+ * attn_bwd_tile_override: for the calling host thread, force the launch
+ * shape of the dK/dV kernel on later attn_bwd calls at d <= 128 (for sweeps
+ * and tests): nkw 32-key blocks per workgroup and hs groups of nkw waves,
+ * each group taking every hs-th (query head, query tile) iteration, with
+ * the groups' dK and dV sums added in LDS at the end.  (4, 1) is the plain
+ * kernel; (4, 2) and (2, 4) are the eight-wave shapes the library takes on
+ * grids of fewer 128-key workgroups than compute units.  (0, 0) returns to
+ * the library's choice; d = 256 always runs (4, 1).  ATTN_ERR_VALUE for any
+ * other pair.
+ */
+attn_status attn_bwd_tile_override(int nkw, int hs);
+
+/*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles
  * created by the caller.  While set (per calling host thread), every entry
  * point binds events[2i] and events[2i+1] (those with index < n) to the i-th

@@ -193,6 +193,16 @@ def test_fwd_tile_entry_points():
     assert aos.attn_fwd_tile_plan(128, True, 1, 2, 2, 65, 64) == (None, [])
 
 
+def test_bwd_tile_override_values():
+    """dK/dV launch shapes: (0, 0), (4, 1), (4, 2) and (2, 4) only."""
+    L = aos.lib()
+    for nkw, hs in ((4, 1), (4, 2), (2, 4), (0, 0)):
+        assert L.attn_bwd_tile_override(nkw, hs) == 0
+    for nkw, hs in ((2, 2), (4, 4), (8, 1), (0, 1), (4, 0), (-4, 1), (1, 8)):
+        assert L.attn_bwd_tile_override(nkw, hs) == VALUE
+    assert L.attn_bwd_tile_override(0, 0) == 0
+
+
 def test_decode_paged_validation():
     f = Fake()
     q, kp, vp, tab, lens, o, lse, ws = (f() for _ in range(8))
