@@ -82,7 +82,7 @@ def lib():
     L.attn_fwd_tile_override.restype = i
     L.attn_fwd_tile_override.argtypes = [i, i, i]
     L.attn_bwd_tile_override.restype = i
-    L.attn_bwd_tile_override.argtypes = [i, i]
+    L.attn_bwd_tile_override.argtypes = [i, i, i, i]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -142,11 +142,12 @@ def attn_fwd_tile_override(nw=0, bc=0, split=1):
         raise AttnError(st, "attn_fwd_tile_override")
 
 
-def attn_bwd_tile_override(nkw=0, hs=0):
-    """Force the dK/dV launch shape (32-key blocks per workgroup, wave
-    groups) on this thread's later backward calls at d <= 128: (4, 1),
-    (4, 2) or (2, 4); (0, 0) returns to the library's choice."""
-    st = lib().attn_bwd_tile_override(int(nkw), int(hs))
+def attn_bwd_tile_override(nkw=0, hs=0, nqw=0, qhs=0):
+    """Force the launch shapes of the backward kernels on this thread's later
+    calls at d <= 128: dK/dV (32-key blocks per workgroup, wave groups) and
+    dQ (32-row blocks per workgroup, wave groups), each (4, 1), (4, 2) or
+    (2, 4); (0, 0) leaves that kernel to the library's choice."""
+    st = lib().attn_bwd_tile_override(int(nkw), int(hs), int(nqw), int(qhs))
     if st:
         raise AttnError(st, "attn_bwd_tile_override")
 

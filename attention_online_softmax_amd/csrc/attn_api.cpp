@@ -83,10 +83,64 @@ thread_local int g_n_events = 0;
 }  // namespace
 
 namespace attn {
-static thread_local int t_dkdv_nkw = 0, t_dkdv_hs = 0;
-void bwd_set_dkdv_override(int nkw, int hs) {
+static thread_local int t_dkdv_nkw = 0, t_dkdv_hs = 0, t_dq_nqw = 0, t_dq_hs = 0;
+void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs) {
   t_dkdv_nkw = nkw;
   t_dkdv_hs = hs;
+  t_dq_nqw = nqw;
+  t_dq_hs = qhs;
+}
+
+// The three shapes' estimated times from the grid's load per compute unit
+// and its longest workgroup (see bwd_dkdv_config): the plain shape's
+// workgroups run two per compute unit, and a heavy one may end alone on
+// its compute unit at one wave per SIMD (chain41 units per iteration);
+// (4, 2) halves a workgroup's iterations over two groups at two waves per
+// SIMD; (2, 4) quarters them over twice as many workgroups.  ovh42 and
+// ovh24 price the grouped shapes' merge and extra loads.  Ties go to the
+// plain shape.  Returns the pick as (blocks per workgroup, groups).
+static void pick_shape(double load, double n_max, double chain41, double ovh42, double ovh24,
+                       int* nb, int* hs) {
+  const double t41 = std::max(load, chain41 * n_max);
+  const double t42 = std::max(ovh42 * load, n_max);
+  const double t24 = std::max(ovh24 * load, 0.5 * n_max);
+  *nb = 4;
+  *hs = 1;
+  if (t42 < t41 && t42 <= t24) {
+    *hs = 2;
+  } else if (t24 < t41 && t24 < t42) {
+    *nb = 2;
+    *hs = 4;
+  }
+}
+
+void bwd_dq_config(const BwdArgs& a, int* nqw, int* hs) {
+  if (t_dq_nqw) {
+    *nqw = t_dq_nqw;
+    *hs = t_dq_hs;
+    return;
+  }
+  // Per 128-row workgroup the iterations are its 32-key blocks: the keys up
+  // to its last row's causal bound, from its first row's window start.
+  const int off = a.Skv - a.Sq;
+  const bool win = a.causal && a.window > 0;
+  const int nq = (a.Sq + 127) / 128;
+  double sum = 0.0;
+  int nb_max = 0;
+  for (int qt = 0; qt < nq; ++qt) {
+    const int last = std::min(qt * 128 + 127, a.Sq - 1);
+    const int kv_end = a.causal ? std::min(a.Skv, last + off + 1) : a.Skv;
+    const int kv_begin = win ? std::max(0, qt * 128 + off - a.window + 1) / 32 * 32 : 0;
+    const int nb = std::max(0, (kv_end - kv_begin + 31) / 32);
+    sum += nb;
+    nb_max = std::max(nb_max, nb);
+  }
+  // Fitted on MI355X: the plain dQ kernel's heavy workgroups run at about
+  // one unit per iteration even alone on a compute unit (chain 1.0), and the
+  // grouped shapes' 32-key tiles (the plain kernel's are 64) cost 15 % at
+  // (4, 2) and 40 % at (2, 4).
+  const double load = sum * a.B * a.Hq / device_cus();
+  pick_shape(load, (double)nb_max, 1.0, 1.15, 1.40, nqw, hs);
 }
 void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
   if (t_dkdv_nkw) {
@@ -123,18 +177,7 @@ void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
     nq_max = std::max(nq_max, nq);
   }
   const double load = sum * a.B * a.Hkv * G / device_cus();
-  const double n_max = (double)nq_max * G;
-  const double t41 = std::max(load, 1.3 * n_max);
-  const double t42 = std::max(1.05 * load, n_max);
-  const double t24 = std::max((G > 1 ? 1.05 : 1.40) * load, 0.5 * n_max);
-  *nkw = 4;
-  *hs = 1;
-  if (t42 < t41 && t42 <= t24) {
-    *hs = 2;
-  } else if (t24 < t41 && t24 < t42) {
-    *nkw = 2;
-    *hs = 4;
-  }
+  pick_shape(load, (double)nq_max * G, 1.3, 1.05, G > 1 ? 1.05 : 1.40, nkw, hs);
 }
 
 void timing_events(int i, hipEvent_t* start, hipEvent_t* stop) {
@@ -171,11 +214,12 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split) {
   return ATTN_OK;
 }
 
-attn_status attn_bwd_tile_override(int nkw, int hs) {
-  const bool ok = (nkw == 0 && hs == 0) || (nkw == 4 && hs == 1) || (nkw == 4 && hs == 2) ||
-                  (nkw == 2 && hs == 4);
-  if (!ok) return ATTN_ERR_VALUE;
-  attn::bwd_set_dkdv_override(nkw, hs);
+attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs) {
+  auto ok = [](int nb, int h) {
+    return (nb == 0 && h == 0) || (nb == 4 && h == 1) || (nb == 4 && h == 2) || (nb == 2 && h == 4);
+  };
+  if (!ok(nkw, hs) || !ok(nqw, qhs)) return ATTN_ERR_VALUE;
+  attn::bwd_set_tile_override(nkw, hs, nqw, qhs);
   return ATTN_OK;
 }
 

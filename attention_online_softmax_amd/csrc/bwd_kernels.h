@@ -442,23 +442,35 @@ struct BwdTile {
 // lane (one query) holds dS^T for 8 contiguous keys per k-step: the B operand
 // of dQ^T += K^T dS^T, whose A operand K^T is a transpose read of the K tile.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WIN, bool BIAS>
-__global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dq_kernel(
+//
+// Small grids: NQW 32-row query blocks per workgroup and HS groups of NQW
+// waves (as in the dK/dV kernel); group h takes the key tiles t0 + h,
+// t0 + h + HS, ... through buffers of its own, and groups 1 .. HS-1 add
+// their dQ sums into group 0's through LDS at the end.  (4, 1) is the plain
+// kernel; the eight-wave shapes (4, 2) and (2, 4) use 32-key tiles.
+template <int D, bool CAUSAL, bool WIN, bool BIAS, int NQW = 4, int HS = 1>
+__global__ __launch_bounds__(64 * NQW * HS, (kBwdMinWaves<D>)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
     const float* __restrict__ LSE, float* __restrict__ ws, uint16_t* __restrict__ dQ, int BH,
     int Hq, int Hkv, int Sq, int Sqp, int Skv, int window, const float* __restrict__ bias,
     int64_t bsb, int64_t bsh, float scale, float scale_log2, int n_qtiles) {
-  constexpr int BC = BwdTile<D>::KB;
+  static_assert((NQW == 4 && HS == 1) || (D <= 128 && NQW * HS == 8),
+                "(4, 1), or eight waves at d <= 128");
+  constexpr int BC = HS == 1 ? BwdTile<D>::KB : 32;
+  constexpr int BR = 32 * NQW;   // query rows per workgroup
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK1[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV1[BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[HS * BC * D];   // one tile per group
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[HS * BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[HS * BC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[HS * BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
+  const int qb = HS == 1 ? wave : wave % NQW;   // the wave's 32-row block, and its index in the group
+  const int hg = HS == 1 ? 0 : wave / NQW;      // its group
+  const int go = hg * BC * D;                   // the group's tile in each buffer
   const int n = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x % BH;
   const int t = blockIdx.x / BH;
@@ -466,26 +478,26 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dq_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / (Hq / Hkv);
   const int off = Skv - Sq;
-  const int wave_row0 = qtile * 128 + wave * 32;
+  const int wave_row0 = qtile * BR + qb * 32;
   const int row = wave_row0 + n;
   const bool valid = row < Sq;
 
   const uint16_t* Kh = K + (int64_t)(b * Hkv + hk) * Skv * D;
   const uint16_t* Vh = V + (int64_t)(b * Hkv + hk) * Skv * D;
-  const int last_row = min(qtile * 128 + 128, Sq) - 1;
+  const int last_row = min(qtile * BR + BR, Sq) - 1;
   const int kv_end = CAUSAL ? min(Skv, last_row + off + 1) : Skv;
   const int n_tiles = (kv_end + BC - 1) / BC;
   // Sliding window of `window` keys (causal only, 0 = none): row i sees
   // keys [i + off - window + 1, i + off]; the loop starts at the first tile
   // the workgroup's first row can see.
   const bool win = WIN;   // instantiated for causal calls with window > 0 only
-  const int t0 = win ? max(0, qtile * 128 + off - window + 1) / BC : 0;
+  const int t0 = win ? max(0, qtile * BR + off - window + 1) / BC : 0;
 
   // K/V tiles through buffer loads; rows past Skv arrive as zeros (masked).
-  TileDma<D, BC, 4> dma;
-  dma.init(wave, lane);
-  dma.load(Kh, Skv, sK0, t0 * BC, wave);
-  dma.load(Vh, Skv, sV0, t0 * BC, wave);
+  TileDma<D, BC, NQW> dma;   // the group's tiles, moved by its NQW waves
+  dma.init(qb, lane);
+  dma.load(Kh, Skv, sK0 + go, (t0 + hg) * BC, qb);
+  dma.load(Vh, Skv, sV0 + go, (t0 + hg) * BC, qb);
 
   const int qrow = min(row, Sq - 1);
   const uint16_t* Qr = Q + ((int64_t)bh * Sq + qrow) * D;
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dq_kernel(
   // probabilities 0, like the padding rows.
   const float lse_row = valid ? LSE[(int64_t)bh * Sq + qrow] : kNegInf;
   const float nl = lse_row != kNegInf ? -lse_row * kLog2e : kNegInf;
-  if (g == 0 && row < Sqp) *(f32x2*)(ws + 2 * ((int64_t)bh * Sqp + row)) = f32x2{dd, nl};
+  if (g == 0 && hg == 0 && row < Sqp) *(f32x2*)(ws + 2 * ((int64_t)bh * Sqp + row)) = f32x2{dd, nl};
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -532,16 +544,20 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dq_kernel(
   row_read_offsets<D>(n, g, r_off);
   tr_read_offsets<D>(lane, t_off);
 
-  auto step = [&](const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV, int tt) {
+  auto step = [&](const uint16_t* cK0, const uint16_t* cV0, uint16_t* nK0, uint16_t* nV0,
+                  int tt) {
     const int k0 = tt * BC;
     wait_vmcnt0();   // this wave's part of tile tt has landed
     lds_barrier();   // ... and every wave's; the other buffers are free
     opaque_offsets<kRowOffs<D>>(r_off);
     opaque_offsets<kTrOffs<D>>(t_off);
-    if (tt + 1 < n_tiles) {
-      dma.load(Kh, Skv, nK, k0 + BC, wave);
-      dma.load(Vh, Skv, nV, k0 + BC, wave);
+    if (tt + HS < n_tiles) {
+      dma.load(Kh, Skv, nK0 + go, k0 + HS * BC, qb);
+      dma.load(Vh, Skv, nV0 + go, k0 + HS * BC, qb);
     }
+    if (HS > 1 && tt >= n_tiles) return;   // the group has no tile left (its last step)
+    const uint16_t* cK = cK0 + go;
+    const uint16_t* cV = cV0 + go;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
       const int ks = k0 + kb * 32;
@@ -610,10 +626,51 @@ __global__ __launch_bounds__(256, (kBwdMinWaves<D>)) void bwd_dq_kernel(
         }
     }
   };
+  if constexpr (HS == 1) {
 #pragma clang loop unroll(disable)
-  for (int tt = t0; tt < n_tiles; tt += 2) {
-    step(sK0, sV0, sK1, sV1, tt);
-    if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
+    for (int tt = t0; tt < n_tiles; tt += 2) {
+      step(sK0, sV0, sK1, sV1, tt);
+      if (tt + 1 < n_tiles) step(sK1, sV1, sK0, sV0, tt + 1);
+    }
+  } else {
+    // Every group takes the same number of steps (barriers), the last one
+    // possibly without a tile.
+    const int n_steps = (max(0, n_tiles - t0) + HS - 1) / HS;
+#pragma clang loop unroll(disable)
+    for (int i = 0; i < n_steps; i += 2) {
+      step(sK0, sV0, sK1, sV1, t0 + hg + HS * i);
+      if (i + 1 < n_steps) step(sK1, sV1, sK0, sV0, t0 + hg + HS * (i + 1));
+    }
+    wait_vmcnt0();   // nothing in flight into LDS
+    // Groups 1 .. HS-1 add their dQ sums into group 0's: eight values per
+    // lane and round, as 32-byte rows per lane of the wave's region.
+    float* red = reinterpret_cast<float*>(sK0);
+#pragma unroll
+    for (int rd = 0; rd < 2 * NDB; ++rd) {
+      lds_barrier();   // the buffers (and the previous round) are no longer read
+      f32x16& A = dqt[rd / 2];
+      const int e0 = 8 * (rd % 2);
+      if (hg > 0) {
+        float* dst = red + ((hg - 1) * NQW + qb) * 512 + lane * 8;
+        *(f32x4*)dst = f32x4{A[e0], A[e0 + 1], A[e0 + 2], A[e0 + 3]};
+        *(f32x4*)(dst + 4) = f32x4{A[e0 + 4], A[e0 + 5], A[e0 + 6], A[e0 + 7]};
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's writes are done
+      lds_barrier();
+      if (hg == 0) {
+#pragma unroll
+        for (int hh = 1; hh < HS; ++hh) {
+          const float* src = red + ((hh - 1) * NQW + qb) * 512 + lane * 8;
+          const f32x4 a = *(const f32x4*)src, c = *(const f32x4*)(src + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            A[e0 + j] += a[j];
+            A[e0 + 4 + j] += c[j];
+          }
+        }
+      }
+    }
+    if (hg > 0) return;
   }
   if (!valid) return;
   store_transposed<NDB>(dQ + ((int64_t)bh * Sq + row) * D, dqt, g, scale);
@@ -625,13 +682,33 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   const int64_t rows_pad = (int64_t)a.B * a.Hq * Sqp;
   const float sl2 = a.scale * kLog2e;
   // dQ first: it also writes the (D, nl) pairs the dK/dV kernel reads.
-  const int n_qtiles = (a.Sq + 127) / 128;
   const int BH = a.B * a.Hq;
-  ATTN_LAUNCH(0, (bwd_dq_kernel<D, CAUSAL, WIN, BIAS>), dim3(n_qtiles * BH), dim3(256), a.stream,
-              (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-              (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws, (uint16_t*)a.dq,
-              BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
-              a.scale, sl2, n_qtiles);
+  auto dq = [&](auto nqw, auto hs) {
+    constexpr int NQW = decltype(nqw)::value, HS = decltype(hs)::value;
+    const int n_qtiles = (a.Sq + 32 * NQW - 1) / (32 * NQW);
+    ATTN_LAUNCH(0, (bwd_dq_kernel<D, CAUSAL, WIN, BIAS, NQW, HS>), dim3(n_qtiles * BH),
+                dim3(64 * NQW * HS), a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const uint16_t*)a.o, a.lse, a.ws,
+                (uint16_t*)a.dq, BH, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias,
+                a.bias_sb, a.bias_sh, a.scale, sl2, n_qtiles);
+  };
+  {
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J4 = std::integral_constant<int, 4>;
+    if constexpr (D <= 128) {
+      int nqw, hs;
+      bwd_dq_config(a, &nqw, &hs);
+      if (nqw == 2 && hs == 4)
+        dq(J2{}, J4{});
+      else if (nqw == 4 && hs == 2)
+        dq(J4{}, J2{});
+      else
+        dq(J4{}, J1{});
+    } else {
+      dq(J4{}, J1{});
+    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BHk = a.B * a.Hkv;

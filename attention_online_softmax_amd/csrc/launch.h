@@ -97,7 +97,10 @@ hipError_t launch_bwd(const BwdArgs& a);
 // (4, 2) / (2, 4) on grids of fewer 128-key workgroups than compute units;
 // and a per-thread override for sweeps and tests ((0, 0) = none).
 void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs);
-void bwd_set_dkdv_override(int nkw, int hs);
+// The same for the dQ kernel: 32-row query blocks per workgroup (nqw) and
+// wave groups that split the key tiles (hs).
+void bwd_dq_config(const BwdArgs& a, int* nqw, int* hs);
+void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs);
 hipError_t launch_bwd_d256(const BwdArgs& a);   // d = 256 (bwd256.hip)
 // Fused variant (no window or bias): ws holds the (D, nl) pairs, then from
 // bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].

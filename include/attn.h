@@ -317,16 +317,17 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split);
 
 /*
  * attn_bwd_tile_override: for the calling host thread, force the launch
- * shape of the dK/dV kernel on later attn_bwd calls at d <= 128 (for sweeps
- * and tests): nkw 32-key blocks per workgroup and hs groups of nkw waves,
- * each group taking every hs-th (query head, query tile) iteration, with
- * the groups' dK and dV sums added in LDS at the end.  (4, 1) is the plain
- * kernel; (4, 2) and (2, 4) are the eight-wave shapes the library takes on
- * grids of fewer 128-key workgroups than compute units.  (0, 0) returns to
- * the library's choice; d = 256 always runs (4, 1).  ATTN_ERR_VALUE for any
- * other pair.
+ * shapes of the two backward kernels on later attn_bwd calls at d <= 128
+ * (for sweeps and tests).  dK/dV: nkw 32-key blocks per workgroup and hs
+ * groups of nkw waves, each group taking every hs-th (query head, query
+ * tile) iteration; dQ: nqw 32-row query blocks per workgroup and qhs groups
+ * of nqw waves, each group taking every qhs-th key tile.  The groups' sums
+ * are added in LDS at the end.  Each pair is (4, 1) (the plain kernel),
+ * (4, 2) or (2, 4) (eight waves, the shapes the library takes on grids too
+ * small to fill the compute units), or (0, 0) for the library's choice;
+ * d = 256 always runs (4, 1).  ATTN_ERR_VALUE for any other pair.
  */
-attn_status attn_bwd_tile_override(int nkw, int hs);
+attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs);
 
 /*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles

@@ -194,13 +194,17 @@ def test_fwd_tile_entry_points():
 
 
 def test_bwd_tile_override_values():
-    """dK/dV launch shapes: (0, 0), (4, 1), (4, 2) and (2, 4) only."""
+    """Backward launch shapes: (0, 0), (4, 1), (4, 2) and (2, 4) only, for
+    dK/dV and for dQ."""
     L = aos.lib()
-    for nkw, hs in ((4, 1), (4, 2), (2, 4), (0, 0)):
-        assert L.attn_bwd_tile_override(nkw, hs) == 0
-    for nkw, hs in ((2, 2), (4, 4), (8, 1), (0, 1), (4, 0), (-4, 1), (1, 8)):
-        assert L.attn_bwd_tile_override(nkw, hs) == VALUE
-    assert L.attn_bwd_tile_override(0, 0) == 0
+    good = ((4, 1), (4, 2), (2, 4), (0, 0))
+    for a in good:
+        for b in good:
+            assert L.attn_bwd_tile_override(*a, *b) == 0
+    for bad in ((2, 2), (4, 4), (8, 1), (0, 1), (4, 0), (-4, 1), (1, 8)):
+        assert L.attn_bwd_tile_override(*bad, 0, 0) == VALUE
+        assert L.attn_bwd_tile_override(0, 0, *bad) == VALUE
+    assert L.attn_bwd_tile_override(0, 0, 0, 0) == 0
 
 
 def test_decode_paged_validation():

@@ -19,11 +19,11 @@ def bwd_plain(*args, **kw):
     fused kernel is that shape with dQ folded in, so their dK and dV agree
     bit for bit (the grouped shapes a small grid may take add the groups'
     sums in another order)."""
-    aos.attn_bwd_tile_override(4, 1)
+    aos.attn_bwd_tile_override(4, 1, 0, 0)
     try:
         return aos.attn_bwd(*args, **kw)
     finally:
-        aos.attn_bwd_tile_override(0, 0)
+        aos.attn_bwd_tile_override(0, 0, 0, 0)
 
 # (B, Hq, Hkv, Sq, Skv, d, causal): ragged query and key tiles, grouped heads,
 # Sq < Skv and Sq > Skv, key tiles shorter than the 128 keys of a workgroup,

@@ -1,8 +1,9 @@
-"""The dK/dV kernel's eight-wave launch shapes for small grids, (4, 2) and
-(2, 4) (32-key blocks per workgroup, groups of waves that split the query
-iterations and add their sums in LDS), forced through
+"""The backward kernels' eight-wave launch shapes for small grids, (4, 2)
+and (2, 4): dK/dV with 32-key blocks per workgroup and groups of waves that
+split the query iterations, dQ with 32-row blocks per workgroup and groups
+that split the key tiles, the groups' sums added in LDS.  Forced through
 attn_bwd_tile_override and checked against the float64 oracle, beside the
-plain (4, 1) shape on the same inputs."""
+plain (4, 1) shapes on the same inputs."""
 import math
 
 import numpy as np
@@ -17,7 +18,9 @@ from tests.test_gpu_bias import make_bias
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(4, 1), (4, 2), (2, 4)]
+# (dK/dV shape, dQ shape)
+SHAPES = [((4, 1), (4, 1)), ((4, 2), (4, 2)), ((2, 4), (2, 4)), ((4, 2), (2, 4)),
+          ((2, 4), (4, 2))]
 
 # (B, Hq, Hkv, Sq, Skv, d, causal, window, bias kind or None)
 CASES = [
@@ -53,42 +56,48 @@ def test_dkdv_shapes_parity(case):
                                              scale, window=W, bias=bf)
     got = {}
     try:
-        for nkw, hs in SHAPES:
-            note(f"bwd dK/dV shape ({nkw}, {hs}) {case}")
-            aos.attn_bwd_tile_override(nkw, hs)
+        for kv, qs in SHAPES:
+            note(f"bwd shapes dK/dV {kv} dQ {qs} {case}")
+            aos.attn_bwd_tile_override(*kv, *qs)
             dq, dk, dv = aos.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
                                       causal=causal, scale=scale, window=W, bias=bg)
             torch.cuda.synchronize()
-            assert_close(to_f64(dq), rq, TOL_GRAD, f"({nkw},{hs}) dQ")
-            assert_close(to_f64(dk), rk, TOL_GRAD, f"({nkw},{hs}) dK")
-            assert_close(to_f64(dv), rv, TOL_GRAD, f"({nkw},{hs}) dV")
-            got[(nkw, hs)] = (dq, dk, dv)
+            assert_close(to_f64(dq), rq, TOL_GRAD, f"{kv}/{qs} dQ")
+            assert_close(to_f64(dk), rk, TOL_GRAD, f"{kv}/{qs} dK")
+            assert_close(to_f64(dv), rv, TOL_GRAD, f"{kv}/{qs} dV")
+            got[(kv, qs)] = (dq, dk, dv)
     finally:
-        aos.attn_bwd_tile_override(0, 0)
-    # dQ comes from the same kernel in every shape: identical bits.
-    for s in SHAPES[1:]:
-        assert torch.equal(got[s][0], got[(4, 1)][0])
+        aos.attn_bwd_tile_override(0, 0, 0, 0)
+    # dK/dV read only the (D, -lse log2 e) pairs from the dQ kernel, which
+    # every dQ shape forms alike: the same dK/dV shape gives the same bits.
+    for kv, q1, q2 in (((4, 2), (4, 2), (2, 4)), ((2, 4), (2, 4), (4, 2))):
+        assert torch.equal(got[(kv, q1)][1], got[(kv, q2)][1])
+        assert torch.equal(got[(kv, q1)][2], got[(kv, q2)][2])
+    # dQ likewise depends only on its own shape.
+    assert torch.equal(got[((4, 2), (2, 4))][0], got[((2, 4), (2, 4))][0])
 
 
-def test_dkdv_shapes_guard_regions():
-    """Nothing is written past dK and dV by the grouped shapes (ragged keys)."""
+def test_bwd_shapes_guard_regions():
+    """Nothing is written past dQ, dK and dV by the grouped shapes (ragged
+    queries and keys)."""
     B, Hq, Hkv, Sq, Skv, d = 1, 8, 1, 200, 170, 128
     dev, _ = inputs(B, Hq, Hkv, Sq, Skv, d, "bf16", 1900, with_do=True)
     o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=False)
-    n = B * Hkv * Skv * d
     pad = 4096
     try:
-        for nkw, hs in SHAPES[1:]:
-            note(f"bwd dK/dV guard ({nkw}, {hs})")
-            aos.attn_bwd_tile_override(nkw, hs)
-            buf_k = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
-            buf_v = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
-            dk = buf_k[pad:pad + n].view(B, Hkv, Skv, d)
-            dv = buf_v[pad:pad + n].view(B, Hkv, Skv, d)
-            aos.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=False, dk=dk,
-                         dv=dv)
+        for kv, qs in SHAPES[1:]:
+            note(f"bwd guard dK/dV {kv} dQ {qs}")
+            aos.attn_bwd_tile_override(*kv, *qs)
+            bufs, views = [], []
+            for shape in ((B, Hq, Sq, d), (B, Hkv, Skv, d), (B, Hkv, Skv, d)):
+                n = shape[0] * shape[1] * shape[2] * shape[3]
+                buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+                bufs.append((buf, n))
+                views.append(buf[pad:pad + n].view(*shape))
+            aos.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=False,
+                         dq=views[0], dk=views[1], dv=views[2])
             torch.cuda.synchronize()
-            for buf in (buf_k, buf_v):
+            for buf, n in bufs:
                 assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
     finally:
-        aos.attn_bwd_tile_override(0, 0)
+        aos.attn_bwd_tile_override(0, 0, 0, 0)
