@@ -659,6 +659,55 @@ def bench_fused_bwd(args, hev, stream, reps):
             "dq_atomic_GB/s_over_fused_kernel": atom / (kern["dkdv_dq_fused_kernel"] * 1e-6) / 1e9}
 
 
+def bench_gqa_bwd(args, hev, stream, reps):
+    """Backward with grouped heads (eight query heads per key/value head),
+    bf16 causal d128 S4096, on two grids smaller than the chip: B4 Hq32 Hkv4
+    (512 128-key workgroups for dK/dV) and B1 Hq32 Hkv4 (128).  Times the
+    library's launch shapes and, for comparison, both kernels forced to the
+    plain (4, 1) shape."""
+    import torch
+    import attention_online_softmax_amd as aos
+    from attention_online_softmax_amd.inputs import make_qkv
+    res = {"workload": "gqa_bwd: bf16 causal Hq32 Hkv4 S4096 d128, backward only, B4 and B1"}
+    for B in (4, 1):
+        Hq, Hkv, S, d = 32, 4, 4096, 128
+        seed = 6000 + B
+        x = {k: v.cuda() for k, v in make_qkv(B, Hq, Hkv, S, S, d, seed=seed,
+                                               with_do=True).items()}
+        scale = d ** -0.5
+        o, lse = aos.attn_fwd(x["q"], x["k"], x["v"], causal=True, scale=scale)
+        g = dict(dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["k"]),
+                 dv=torch.empty_like(x["v"]),
+                 ws=torch.empty(aos.attn_bwd_workspace_bytes(B, Hq, S, d), device="cuda",
+                                dtype=torch.uint8))
+
+        def bwd(i):
+            aos.attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=True, scale=scale,
+                         dq=g["dq"], dk=g["dk"], dv=g["dv"], workspace=g["ws"])
+
+        out = {"seed": seed}
+        for name, shape in (("picked", (0, 0, 0, 0)), ("plain", (4, 1, 4, 1))):
+            aos.attn_bwd_tile_override(*shape)
+            try:
+                for i in range(2):
+                    bwd(i)
+                torch.cuda.synchronize()
+                _, times, spans = run_calls([("bwd", bwd)], {"bwd": 2}, hev, reps, stream)
+            finally:
+                aos.attn_bwd_tile_override(0, 0, 0, 0)
+            q = quantiles([t for t in spans["bwd"] if t is not None])
+            kq = quantiles([t[0] for t in times["bwd"]])["median"]
+            kk = quantiles([t[1] for t in times["bwd"]])["median"]
+            flop = 10 * d * B * Hq * S * (S + 1) / 2   # 2.5 x the forward's 4 d per pair
+            tf = flop / (q["median"] * 1e-3) / 1e12
+            out[name] = {"us": q["median"] * 1e3, "dq_kernel_us": kq * 1e3,
+                         "dkdv_kernel_us": kk * 1e3, "TFLOP/s": tf,
+                         "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+        del x, o, lse, g
+        res[f"B{B}"] = out
+    return res
+
+
 def measured_ceilings(stream):
     """What the box reaches, as the measured ceilings beside the spec peaks:
     HBM read bandwidth of a grid-stride streaming read of 1 GiB (three
@@ -890,7 +939,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill", "small",
-                                       "tiles"], default=None)
+                                       "tiles", "gqa_bwd"], default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -927,6 +976,9 @@ def main():
     if args.only == "tiles":
         print(json.dumps(bench_tile_selection(args, hev, stream)), flush=True)
         return
+    if args.only == "gqa_bwd":
+        print(json.dumps(bench_gqa_bwd(args, hev, stream, args.steps)), flush=True)
+        return
 
     w, cpu0, r = bench_fwd_bwd(args, hev, stream)
     print(f"[bench] fwd+bwd: {r['ms_per_step']:.3f} ms/step, {r['value']:.1f} TFLOP/s",
@@ -949,6 +1001,11 @@ def main():
         extras["fused_bwd"] = bench_fused_bwd(args, hev, stream, max(args.steps, 20))
         print(f"[bench] backward two-kernel {extras['fused_bwd']['two_kernel_us']:.1f} us, "
               f"fused {extras['fused_bwd']['fused_us']:.1f} us", file=sys.stderr, flush=True)
+        extras["gqa_bwd"] = bench_gqa_bwd(args, hev, stream, max(3, min(args.steps, 10)))
+        print("[bench] grouped-head backward: " + ", ".join(
+            f"B{b} {extras['gqa_bwd'][f'B{b}']['picked']['us']:.0f} us (plain shapes "
+            f"{extras['gqa_bwd'][f'B{b}']['plain']['us']:.0f} us)" for b in (4, 1)),
+            file=sys.stderr, flush=True)
         extras["small_fwd"] = bench_small(args, hev, stream, max(args.steps, 50))
         print(f"[bench] fp32 S128 fwd {extras['small_fwd']['fp32_small']['us_median']:.1f} us, "
               f"block fwd {extras['small_fwd']['block_fwd']['us_median']:.1f} us",
