@@ -75,7 +75,7 @@ def lib():
     L.attn_bwd_fused_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_bwd_fused.restype = i
     L.attn_bwd_fused.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                 i, i, i, i, i, i, i, f, vp, sz, vp]
+                                 i, i, i, i, i, i, i, i, vp, i64, i64, f, vp, sz, vp]
     ip, fp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)
     L.attn_fwd_tile_plan.restype = i
     L.attn_fwd_tile_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, ip, fp, ip]
@@ -345,9 +345,9 @@ def attn_bwd_fused_workspace_bytes(B, Hq, Sq, d):
 
 
 def attn_bwd_fused(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
-                   workspace=None, stream=None):
-    """Fused backward (dQ through fp32 atomic adds; no window or bias).
-    Returns (dq, dk, dv)."""
+                   workspace=None, stream=None, window=0, bias=None):
+    """Fused backward (dQ through fp32 atomic adds; window and bias as in
+    attn_bwd).  Returns (dq, dk, dv)."""
     _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -361,8 +361,9 @@ def attn_bwd_fused(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=No
         workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
     st = lib().attn_bwd_fused(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                               _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
-                              int(bool(causal)), float(scale), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(),
+                              int(bool(causal)), int(window),
+                              *_bias_args(bias, B, Hq, Sq, Skv, q.device), float(scale),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream, q.device))
     if st:
         raise AttnError(st, "attn_bwd_fused")

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxSplits = 256;
 
 struct Span {
@@ -484,17 +484,22 @@ size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d) {
 
 attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* v, const void* o,
                            const void* d_o, const float* lse, void* dq, void* dk, void* dv, int B,
-                           int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+                           int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
+                           const float* bias, int64_t bias_sb, int64_t bias_sh, float scale,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (window > 0 && !causal) return ATTN_ERR_VALUE;
   if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
   // The (D, nl) pairs are addressed with 32-bit byte offsets.
   if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
   if (!bwd_fused_d_ok(dtype, d)) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  int64_t bias_bytes = 0;
+  attn_status st = check_bias(bias, bias_sb, bias_sh, B, Hq, Sq, Skv, &bias_bytes);
+  if (st != ATTN_OK) return st;
   if (!workspace) return ATTN_ERR_WORKSPACE;
   const size_t ws_need = attn_bwd_fused_workspace_bytes(B, Hq, Sq, d);
   if (workspace_bytes < ws_need) return ATTN_ERR_WORKSPACE;
@@ -503,14 +508,15 @@ attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* 
     return ATTN_ERR_ALIGN;
   const int es = esize(dtype);
   const int64_t nq = (int64_t)B * Hq * Sq * d * es, nkv = (int64_t)B * Hkv * Skv * d * es;
-  const Span ins[6] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
-                       span(lse, (int64_t)B * Hq * Sq * 4)};
+  const Span ins[7] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
+                       span(lse, (int64_t)B * Hq * Sq * 4), span(bias, bias_bytes)};
   const Span outs[4] = {span(dq, nq), span(dk, nkv), span(dv, nkv),
                         span(workspace, (int64_t)ws_need)};
-  const attn_status st = check_alias(outs, 4, ins, 6);
+  st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
   attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
-                  causal ? 1 : 0, 0, nullptr, 0, 0, scale, (float*)workspace, (hipStream_t)stream};
+                  causal ? 1 : 0, window > 0 && window < Skv ? window : 0, bias, bias_sb, bias_sh,
+                  scale, (float*)workspace, (hipStream_t)stream};
   return hip_status(attn::launch_bwd_fused(a));
 }
 

@@ -309,8 +309,11 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
 #pragma unroll
     for (int c = 0; c < KW / 16; ++c) {
       const int kr = kb0 + 16 * c;
-      // Keys of a wave that skipped this tile have no dS staged.
-      if (CAUSAL && qs + QT - 1 + off < ktile * 128 + (kr & ~31)) continue;
+      // Keys of a wave that skipped this tile have no dS staged (the skip
+      // test of the loop body, for the wave that owns keys kr).
+      const int kw0 = ktile * 128 + (kr & ~31);
+      if (CAUSAL && qs + QT - 1 + off < kw0) continue;
+      if (win && qs + off - window + 1 > kw0 + 31) continue;
       const u32x4 a = *(const u32x4*)(sS + n * SSTR + kr + 8 * g);
       acc = mfma32(a, tr_col8<D>(sV + kr * D, t_off, qdb), acc);
     }

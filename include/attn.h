@@ -256,7 +256,7 @@ size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d);
 
 /*
  * Fused backward: the gradients of attn_bwd (same formulas and arguments,
- * without window and bias) from one pass over the key tiles: the fused
+ * window and bias included) from one pass over the key tiles: the fused
  * kernel form of the backward that "Tang, a compiler that derives GPU
  * kernels and bounds how fast they can run" reports for CUDA in its Abstract
  * (a flash-style backward with no intermediates written, computing in bf16
@@ -276,7 +276,8 @@ attn_status attn_bwd_fused(int dtype, const void* q, const void* k, const void* 
                            const void* o, const void* d_o, const float* lse,
                            void* dq, void* dk, void* dv,
                            int B, int Hq, int Hkv, int Sq, int Skv, int d,
-                           int causal, float scale,
+                           int causal, int window, const float* bias, int64_t bias_sb,
+                           int64_t bias_sh, float scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*

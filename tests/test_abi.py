@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert aos.attn_abi_version() == 3
+    assert aos.attn_abi_version() == 4
     for s in range(9):
         assert aos.attn_status_str(s) and aos.attn_status_str(s) != "unknown status"
     assert aos.attn_status_str(99) == "unknown status"
@@ -289,12 +289,13 @@ def test_bwd_fused_validation():
 
     def call(**kw):
         a = dict(p)
-        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, scale=0.1,
-                      wsb=need))
+        a.update(dict(dt=BF16, B=1, Hq=4, Hkv=2, Sq=64, Skv=64, d=128, causal=1, window=0,
+                      bias=None, sb=0, sh=0, scale=0.1, wsb=need))
         a.update(kw)
         return L.attn_bwd_fused(a["dt"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
                                 a["dq"], a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
-                                a["Skv"], a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], None)
+                                a["Skv"], a["d"], a["causal"], a["window"], a["bias"], a["sb"],
+                                a["sh"], a["scale"], a["ws"], a["wsb"], None)
 
     for n in names[:-1]:
         assert call(**{n: None}) == NULL, n
@@ -311,6 +312,9 @@ def test_bwd_fused_validation():
     assert call(ws=p["lse"]) == ALIAS
     assert call(dv=p["dv"] + 2) == ALIGN
     assert call(ws=p["ws"] + 8) == ALIGN
+    assert call(causal=0, window=16) == VALUE   # a window needs the causal mask
+    assert call(bias=f(), sb=-8) == VALUE
+    assert call(bias=p["dq"]) == ALIAS           # dQ written over the bias read
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -3,6 +3,7 @@ with the float64 oracle, agreement with the two-kernel backward, and how far
 its run-to-run results differ."""
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -65,6 +66,45 @@ def test_bwd_fused_parity(case):
     _, dk2, dv2 = bwd_plain(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal,
                                scale=scale)
     torch.cuda.synchronize()
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+# (B, Hq, Hkv, Sq, Skv, d, causal, window, bias kind or None)
+MASKED = [
+    (1, 4, 2, 150, 150, 128, True, 40, None),
+    (1, 2, 1, 130, 200, 64, True, 33, None),
+    (1, 4, 2, 100, 160, 64, False, 0, "head1"),
+    (1, 2, 2, 128, 128, 128, True, 0, "full"),
+    (1, 4, 1, 96, 96, 128, True, 33, "shared"),
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "B{}_Hq{}_Hkv{}_Sq{}_Skv{}_d{}_{}_w{}_{}".format(
+    *c[:6], "causal" if c[6] else "full", c[7], c[8] or "nobias"))
+def test_bwd_fused_window_bias(case):
+    """The fused backward with a sliding window and an additive bias (a dead
+    row included) against the oracle; dK and dV bit for bit equal to the
+    two-kernel backward's plain shape."""
+    from tests.test_gpu_bias import make_bias
+    B, Hq, Hkv, Sq, Skv, d, causal, W, kind = case
+    dev, ref = inputs(B, Hq, Hkv, Sq, Skv, d, "bf16", 2100 + sum(case[:6]), with_do=True)
+    scale = 1 / math.sqrt(d)
+    bias = make_bias(kind, B, Hq, Sq, Skv, 2200 + sum(case[:6])) if kind else None
+    bg = bias.cuda() if kind else None
+    note(f"fused bwd masked {case}")
+    o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale, window=W,
+                          bias=bg)
+    dq, dk, dv = aos.attn_bwd_fused(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
+                                    causal=causal, scale=scale, window=W, bias=bg)
+    _, dk2, dv2 = bwd_plain(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal,
+                            scale=scale, window=W, bias=bg)
+    torch.cuda.synchronize()
+    bf = (np.broadcast_to(bias.numpy().astype(np.float64), (B, Hq, Sq, Skv)) if kind else None)
+    rq, rk, rv, _ = oracle.attention_bwd_ref(ref["q"], ref["k"], ref["v"], ref["do"], causal,
+                                             scale, window=W, bias=bf)
+    assert_close(to_f64(dq), rq, TOL_GRAD, "fused masked dQ")
+    assert_close(to_f64(dk), rk, TOL_GRAD, "fused masked dK")
+    assert_close(to_f64(dv), rv, TOL_GRAD, "fused masked dV")
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
