@@ -24,7 +24,8 @@ STATUS_NAMES = {
 }
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
-           "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_fused_workspace_bytes",
+           "attn_bwd_workspace_bytes", "attn_bwd_split_workspace_bytes", "attn_bwd",
+           "attn_bwd_fused_workspace_bytes",
            "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc",
            "attn_fwd_tile_plan", "attn_fwd_tile_override", "attn_bwd_tile_override")
 SCRATCH_BYTES = 8 << 20   # ATTN_SCRATCH_BYTES of attn.h
@@ -82,7 +83,9 @@ def lib():
     L.attn_fwd_tile_override.restype = i
     L.attn_fwd_tile_override.argtypes = [i, i, i]
     L.attn_bwd_tile_override.restype = i
-    L.attn_bwd_tile_override.argtypes = [i, i, i, i]
+    L.attn_bwd_tile_override.argtypes = [i, i, i, i, i]
+    L.attn_bwd_split_workspace_bytes.restype = sz
+    L.attn_bwd_split_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -142,12 +145,13 @@ def attn_fwd_tile_override(nw=0, bc=0, split=1):
         raise AttnError(st, "attn_fwd_tile_override")
 
 
-def attn_bwd_tile_override(nkw=0, hs=0, nqw=0, qhs=0):
+def attn_bwd_tile_override(nkw=0, hs=0, nqw=0, qhs=0, hsplit=0):
     """Force the launch shapes of the backward kernels on this thread's later
-    calls at d <= 128: dK/dV (32-key blocks per workgroup, wave groups) and
-    dQ (32-row blocks per workgroup, wave groups), each (4, 1), (4, 2) or
-    (2, 4); (0, 0) leaves that kernel to the library's choice."""
-    st = lib().attn_bwd_tile_override(int(nkw), int(hs), int(nqw), int(qhs))
+    calls: dK/dV (32-key blocks per workgroup, wave groups) and dQ (32-row
+    blocks per workgroup, wave groups), each (4, 1), (4, 2) or (2, 4) at
+    d <= 128, and the dK/dV head split (1 to 8 workgroups per key tile);
+    zeros leave each to the library's choice."""
+    st = lib().attn_bwd_tile_override(int(nkw), int(hs), int(nqw), int(qhs), int(hsplit))
     if st:
         raise AttnError(st, "attn_bwd_tile_override")
 
@@ -327,8 +331,10 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = attn_bwd_workspace_bytes(B, Hq, Sq, d)
     if workspace is None:
+        # the size that lets the library split grouped heads when it wants to
+        need = (attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, causal)
+                if window == 0 and bias is None else attn_bwd_workspace_bytes(B, Hq, Sq, d))
         workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
     st = lib().attn_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                         _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, d,
@@ -338,6 +344,10 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
     if st:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, causal):
+    return int(lib().attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, int(bool(causal))))
 
 
 def attn_bwd_fused_workspace_bytes(B, Hq, Sq, d):

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxSplits = 256;
 
 struct Span {
@@ -83,12 +83,14 @@ thread_local int g_n_events = 0;
 }  // namespace
 
 namespace attn {
-static thread_local int t_dkdv_nkw = 0, t_dkdv_hs = 0, t_dq_nqw = 0, t_dq_hs = 0;
-void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs) {
+static thread_local int t_dkdv_nkw = 0, t_dkdv_hs = 0, t_dq_nqw = 0, t_dq_hs = 0,
+                        t_hsplit = 0;
+void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs, int hsplit) {
   t_dkdv_nkw = nkw;
   t_dkdv_hs = hs;
   t_dq_nqw = nqw;
   t_dq_hs = qhs;
+  t_hsplit = hsplit;
 }
 
 // The three shapes' estimated times from the grid's load per compute unit
@@ -142,13 +144,32 @@ void bwd_dq_config(const BwdArgs& a, int* nqw, int* hs) {
   const double load = sum * a.B * a.Hq / device_cus();
   pick_shape(load, (double)nb_max, 1.0, 1.15, 1.40, nqw, hs);
 }
-void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
-  if (t_dkdv_nkw) {
-    *nkw = t_dkdv_nkw;
-    *hs = t_dkdv_hs;
-    return;
-  }
-  // Estimated time of each shape, in units of one wave's pass over one
+int64_t bwd_split_part_offset(int B, int Hq, int Sq) {
+  const int64_t sqp = ((int64_t)Sq + 31) / 32 * 32;
+  return (2 * (int64_t)B * Hq * sqp + 63) / 64 * 64;   // the pairs, rounded to 256 bytes
+}
+
+size_t bwd_split_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int d, int p) {
+  const size_t pairs = ((size_t)bwd_split_part_offset(B, Hq, Sq)) * sizeof(float);
+  if (p <= 1) return pairs;
+  return round256(pairs + (size_t)p * 2 * B * Hkv * Skv * d * sizeof(float));
+}
+
+void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs, int* hsplit) {
+  const bool plain = a.window == 0 && !a.bias;
+  auto fits = [&](int p) {
+    return a.ws_bytes >= bwd_split_workspace_bytes(a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.d, p);
+  };
+  // A forced shape or split (attn_bwd_tile_override) is taken as it is; a
+  // forced split the workspace cannot hold is reported by attn_bwd.  d = 256
+  // has only the plain shape; masked calls do not split.
+  const int forced_p = plain ? t_hsplit : (t_hsplit ? 1 : 0);
+  const bool forced_shape = t_dkdv_nkw != 0 && a.d <= 128;
+  *nkw = forced_shape ? t_dkdv_nkw : 4;
+  *hs = forced_shape ? t_dkdv_hs : 1;
+  *hsplit = forced_p ? forced_p : 1;
+  if ((forced_shape || a.d > 128) && forced_p) return;
+  // Estimated time of each launch, in units of one wave's pass over one
   // query iteration (query head, 32-row query tile) of its 32-key block:
   // the larger of the grid's load per compute unit and the longest
   // workgroup.  Per 128 keys the iterations are the query tiles that can
@@ -162,7 +183,18 @@ void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
   // merge and, with 64 keys per workgroup, for loading every Q / dO tile
   // twice as often: 5 % for (4, 2); for (2, 4) 5 % with grouped heads and
   // 40 % without (measured on MI355X: short iteration lists amortise the
-  // per-workgroup costs worst).  Ties go to the plain kernel.
+  // per-workgroup costs worst).  At d = 256 only the plain shape exists,
+  // one wave per SIMD, whose long chains run at about 0.75 load units per
+  // iteration.
+  //   At d <= 128 a tail of 0.1 times the longest workgroup's chain is
+  //   added: the last workgroups leave compute units idle, and the grids
+  //   with shorter workgroups measure faster even where the load bounds
+  //   them.  A head split over p workgroups per key tile divides n_max by
+  //   p (each takes every p-th query head) and adds its float32 partials:
+  //   their writes hide under the kernel's arithmetic, the reduce reads
+  //   them back (8 p bytes per dK/dV element) at about 5.5 TB/s, plus its
+  //   launch; a unit is about 1.15 d/128 us (d <= 128) or 2.9 us (d = 256)
+  //   to weigh them.  Ties go to the plain kernel and to fewer shares.
   const int G = a.Hq / a.Hkv;
   const int off = a.causal ? a.Skv - a.Sq : a.Skv;
   const bool win = a.causal && a.window > 0;
@@ -177,7 +209,32 @@ void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs) {
     nq_max = std::max(nq_max, nq);
   }
   const double load = sum * a.B * a.Hkv * G / device_cus();
-  pick_shape(load, (double)nq_max * G, 1.3, 1.05, G > 1 ? 1.05 : 1.40, nkw, hs);
+  const double unit_us = a.d > 128 ? 2.9 : 1.15 * a.d / 128.0;
+  const double nkv = (double)a.B * a.Hkv * a.Skv * a.d;
+  const double tail = a.d > 128 ? 0.0 : 0.1;
+  double best = INFINITY;
+  for (int p = 1; p <= 8; p *= 2) {
+    if (forced_p && p != forced_p) continue;
+    if (!forced_p && p > 1 && (!plain || p > G || !fits(p))) break;
+    const double gl = std::ceil((double)G / p);   // query heads per workgroup
+    const double n_max = gl * nq_max;
+    const double extra = p > 1 ? (3.0 + 8.0 * p * nkv / 5.5e6) / unit_us : 0.0;
+    struct Shape { int nkw, hs; double ovh, chain; };
+    const Shape shapes[3] = {{4, 1, 1.0, a.d > 128 ? 0.75 : 1.3},
+                             {4, 2, 1.05, 1.0},
+                             {2, 4, gl > 1 ? 1.05 : 1.40, 0.5}};
+    for (int si = 0; si < (a.d > 128 ? 1 : 3); ++si) {
+      const Shape& sh = shapes[si];
+      if (forced_shape && (sh.nkw != t_dkdv_nkw || sh.hs != t_dkdv_hs)) continue;
+      const double t = std::max(sh.ovh * load, sh.chain * n_max) + tail * sh.chain * n_max + extra;
+      if (t < best * 0.999) {
+        best = t;
+        *nkw = sh.nkw;
+        *hs = sh.hs;
+        *hsplit = p;
+      }
+    }
+  }
 }
 
 void timing_events(int i, hipEvent_t* start, hipEvent_t* stop) {
@@ -214,12 +271,12 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split) {
   return ATTN_OK;
 }
 
-attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs) {
+attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs, int hsplit) {
   auto ok = [](int nb, int h) {
     return (nb == 0 && h == 0) || (nb == 4 && h == 1) || (nb == 4 && h == 2) || (nb == 2 && h == 4);
   };
-  if (!ok(nkw, hs) || !ok(nqw, qhs)) return ATTN_ERR_VALUE;
-  attn::bwd_set_tile_override(nkw, hs, nqw, qhs);
+  if (!ok(nkw, hs) || !ok(nqw, qhs) || hsplit < 0 || hsplit > 8) return ATTN_ERR_VALUE;
+  attn::bwd_set_tile_override(nkw, hs, nqw, qhs, hsplit);
   return ATTN_OK;
 }
 
@@ -462,18 +519,37 @@ attn_status attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
     return ATTN_ERR_ALIGN;
+  attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
+                  causal ? 1 : 0, window > 0 && window < Skv ? window : 0, bias, bias_sb, bias_sh, scale,
+                  (float*)workspace, (hipStream_t)stream, workspace_bytes};
+  // The workspace the call will use: the pairs, plus the head split's
+  // partials when it splits (the split it picks fits the workspace given;
+  // a forced one that does not is an error).
+  int nkw = 4, hs = 1, hsplit = 1;
+  if (d <= 256) attn::bwd_dkdv_config(a, &nkw, &hs, &hsplit);
+  const size_t ws_used = attn::bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, hsplit);
+  if (workspace_bytes < ws_used) return ATTN_ERR_WORKSPACE;
   const int es = esize(dtype);
   const int64_t nq = (int64_t)B * Hq * Sq * d * es, nkv = (int64_t)B * Hkv * Skv * d * es;
   const Span ins[7] = {span(q, nq), span(k, nkv), span(v, nkv), span(o, nq), span(d_o, nq),
                        span(lse, (int64_t)B * Hq * Sq * 4), span(bias, bias_bytes)};
   const Span outs[4] = {span(dq, nq), span(dk, nkv), span(dv, nkv),
-                        span(workspace, (int64_t)attn_bwd_workspace_bytes(B, Hq, Sq, d))};
+                        span(workspace, (int64_t)ws_used)};
   st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
-  attn::BwdArgs a{dtype, q, k, v, o, d_o, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d,
-                  causal ? 1 : 0, window > 0 && window < Skv ? window : 0, bias, bias_sb, bias_sh, scale,
-                  (float*)workspace, (hipStream_t)stream};
   return hip_status(attn::launch_bwd(a));
+}
+
+size_t attn_bwd_split_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                                      int causal) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
+  if (causal && Sq > Skv) return 0;
+  attn::BwdArgs a{ATTN_BF16, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0, 0, nullptr, 0, 0,
+                  1.f, nullptr, nullptr, (size_t)-1};
+  int nkw = 4, hs = 1, hsplit = 1;
+  attn::bwd_dkdv_config(a, &nkw, &hs, &hsplit);
+  return attn::bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, hsplit);
 }
 
 size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d) {

@@ -35,7 +35,7 @@ static hipError_t launch_dkdv_fused_t(const BwdArgs& a, float* dqacc) {
               (const uint16_t*)a.v, (const uint16_t*)a.d_o, (const float*)a.ws,
               (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window,
               a.bias, a.bias_sb, a.bias_sh, a.scale, a.scale * kLog2e, rows_pad,
-              a.Skv - a.Sq, dqacc);
+              a.Skv - a.Sq, dqacc, 1, nullptr);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@
 // accumulator before it, another scales and rounds dQ to bf16 after it.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -43,6 +44,20 @@ __device__ __forceinline__ void store_transposed(uint16_t* rowp, const f32x16* a
       u32x2 w = {pack_bf16x2(acc[db][4 * i4] * mul, acc[db][4 * i4 + 1] * mul),
                  pack_bf16x2(acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul)};
       *(u32x2*)(rowp + d0) = w;
+    }
+}
+
+// The same for a float32 destination (partial sums): 16 bytes per store.
+template <int NDB>
+__device__ __forceinline__ void store_transposed_f32(float* rowp, const f32x16* acc, int g,
+                                                     float mul) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = db * 32 + 8 * i4 + 4 * g;
+      *(f32x4*)(rowp + d0) = f32x4{acc[db][4 * i4] * mul, acc[db][4 * i4 + 1] * mul,
+                                   acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul};
     }
 }
 
@@ -80,16 +95,25 @@ constexpr int kBwdMinWaves = D >= 256 ? 1 : 2;
 // the end groups 1 .. HS-1 add their dK/dV sums into group 0's through LDS.
 // (NKW, HS) = (4, 1) is the plain kernel; (4, 2) and (2, 4) run eight waves,
 // two per SIMD, on the same number of keys or half of them.
-template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED, int NKW = 4, int HS = 1>
+//
+// PS (head split, plain calls only): the G query heads of a key/value head
+// are dealt over `hsplit` workgroups per key tile (workgroup p takes heads
+// p, p + hsplit, ...), each of which writes its float32 sums of dK (times
+// scale) and dV to part[p][0 | 1][B, Hkv, Skv, d]; bwd_dkdv_reduce_kernel
+// adds the partials and rounds them to dK and dV.
+template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED, int NKW = 4, int HS = 1,
+          bool PS = false>
 __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
     const float* __restrict__ bias, int64_t bsb, int64_t bsh, float scale, float scale_log2,
-    int64_t rows_pad, int diag, float* __restrict__ dqacc) {
+    int64_t rows_pad, int diag, float* __restrict__ dqacc, int hsplit,
+    float* __restrict__ part) {
   static_assert((NKW == 4 && HS == 1) || (!FUSED && D <= 128 && NKW * HS == 8 &&
                                           (HS - 1) * NKW <= 2 * HS),
                 "(4, 1), or eight waves of a plain kernel at d <= 128");
+  static_assert(!PS || (!FUSED && !WIN && !BIAS), "head split: plain calls only");
   constexpr int NW = NKW * HS;   // waves per workgroup
   constexpr int KT = 32 * NKW;   // keys per workgroup
   constexpr int QT = 32;   // query rows per tile
@@ -113,10 +137,16 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   const int kbw = HS == 1 ? wave : wave % NKW;   // the wave's key block, and its index in the group
   const int hg = HS == 1 ? 0 : wave / NKW;       // its group
   const int n = lane & 31, g = lane >> 5;
-  const int bhk = blockIdx.x % BHk;
-  const int ktile = blockIdx.x / BHk;
+  const int pidx = PS ? (int)(blockIdx.x % (unsigned)hsplit) : 0;   // head split share
+  const int wg = PS ? (int)(blockIdx.x / (unsigned)hsplit) : (int)blockIdx.x;
+  const int bhk = wg % BHk;
+  const int ktile = wg / BHk;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int G = Hq / Hkv;
+  // Query heads of this workgroup: all G, or (PS) G / hsplit of them; head
+  // index hh of the loop is query head hk G + head(hh).
+  const int Gl = PS ? (G - pidx + hsplit - 1) / hsplit : G;
+  auto head = [&](int hh) { return PS ? pidx + hsplit * hh : hh; };
   const int off = diag;   // key j is visible to query i iff j <= i + off (causal)
   const int key0_wave = ktile * KT + kbw * 32;
   // Lane n owns key swap23(n) of the wave's 32: the V rows it needs as the
@@ -136,7 +166,7 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   // Query tiles per head; 0 when no query's window reaches these keys
   // (possible only with a window and Sq < Skv).
   const int n_qt = max(0, (q_end - q_start + QT - 1) / QT);
-  const int n_it = G * n_qt;
+  const int n_it = Gl * n_qt;
 
   // The workgroup's V rows, K rows when FUSED (rows past Skv arrive as zeros).
   {
@@ -155,7 +185,7 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   // fetched.  Iterations advance by HS: (hh, qt) moves HS tiles on.
   auto advance = [&](int& hh, int& qt, int by) {
     qt += by;
-    while (qt >= n_qt && hh < G) {   // at most HS passes (n_qt >= 1 when it matters)
+    while (qt >= n_qt && hh < Gl) {   // at most HS passes (n_qt >= 1 when it matters)
       qt -= n_qt;
       ++hh;
     }
@@ -163,13 +193,13 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   int dma_hh = 0, dma_qt = 0;
   if constexpr (HS > 1) {
     if (n_qt > 0) advance(dma_hh, dma_qt, hg);
-    else dma_hh = G;
+    else dma_hh = Gl;
   }
   auto issue = [&](uint16_t* slot0) {
-    if (dma_hh >= G) return;
+    if (dma_hh >= Gl) return;
     uint16_t* slot = slot0 + hg * SLOT;
     const int q0 = q_start + dma_qt * QT;
-    const int64_t bh = (int64_t)b * Hq + hk * G + dma_hh;
+    const int64_t bh = (int64_t)b * Hq + hk * G + head(dma_hh);
     if (kbw == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ws_rs, (__attribute__((address_space(3))) void*)(slot + 2 * QT * D), 4, lane * 4,
@@ -339,7 +369,7 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   int cur_qt = 0, cur_hh = 0;   // query tile and query head of the group's next step
   if constexpr (HS > 1) {
     if (n_qt > 0) advance(cur_hh, cur_qt, hg);
-    else cur_hh = G;
+    else cur_hh = Gl;
   }
   auto body = [&](const uint16_t* cur0, uint16_t* nxt) {
     wait_vmcnt0();   // this wave's part of the current tile (and V) has landed
@@ -349,14 +379,14 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
     issue(nxt);
     const uint16_t* cur = cur0 + hg * SLOT;
     const int qs = q_start + cur_qt * QT;
-    const int hh = cur_hh;
+    const int hh = head(cur_hh);
     if constexpr (HS == 1) {
       if (++cur_qt == n_qt) {
         cur_qt = 0;
         ++cur_hh;
       }
     } else {
-      if (hh >= G) return;   // the group has no iteration left (the last step)
+      if (cur_hh >= Gl) return;   // the group has no iteration left (the last step)
       advance(cur_hh, cur_qt, HS);
     }
     // Tiles whose queries all precede this wave's first visible key, or
@@ -423,8 +453,44 @@ __global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_ker
   }
   if (!kvalid) return;
   const int64_t kro = ((int64_t)(b * Hkv + hk) * Skv + key) * D;
-  store_transposed<NDB>(dK + kro, dkt, g, scale);
-  store_transposed<NDB>(dV + kro, dvt, g, 1.f);
+  if constexpr (PS) {
+    const int64_t nkv = (int64_t)BHk * Skv * D;
+    store_transposed_f32<NDB>(part + 2 * pidx * nkv + kro, dkt, g, scale);
+    store_transposed_f32<NDB>(part + (2 * pidx + 1) * nkv + kro, dvt, g, 1.f);
+  } else {
+    store_transposed<NDB>(dK + kro, dkt, g, scale);
+    store_transposed<NDB>(dV + kro, dvt, g, 1.f);
+  }
+}
+
+// dK and dV of the head split: the sum of the hsplit partials, in order,
+// rounded to bf16.  Eight elements per thread and step.  (A template on the
+// head dimension only so that each source including this header names its
+// own instantiation.)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ dK,
+                                                              uint16_t* __restrict__ dV,
+                                                              int64_t nkv, int hsplit) {
+  const int64_t n8 = nkv / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n8;
+       i += (int64_t)gridDim.x * 256) {
+    const int t = i >= n8;   // 0: dK, 1: dV
+    const int64_t e = (i - t * n8) * 8;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < hsplit; ++p) {
+      const float* src = part + (2 * p + t) * nkv + e;
+      const f32x4 x = *(const f32x4*)src, y = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[j] += x[j];
+        c[j] += y[j];
+      }
+    }
+    const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(c[0], c[1]),
+                     pack_bf16x2(c[2], c[3])};
+    *(u32x4*)((t ? dV : dK) + e) = w;
+  }
 }
 
 template <int D>
@@ -721,30 +787,60 @@ static hipError_t launch_bwd_w(const BwdArgs& a) {
   // fit the registers of that head dimension and spills.
   constexpr bool AS_CAUSAL = CAUSAL || (D >= 256 && !WIN);
   const int diag = CAUSAL ? a.Skv - a.Sq : a.Skv;
-  auto dkdv = [&](auto nkw, auto hs) {
-    constexpr int NKW = decltype(nkw)::value, HS = decltype(hs)::value;
+  int nkw = 4, hs = 1, hsplit = 1;
+  bwd_dkdv_config(a, &nkw, &hs, &hsplit);
+  // Head split: float32 partials after the (D, nl) pairs in the workspace.
+  float* part = a.ws + bwd_split_part_offset(a.B, a.Hq, a.Sq);
+  auto dkdv = [&](auto nkw_c, auto hs_c, auto ps_c) {
+    constexpr int NKW = decltype(nkw_c)::value, HS = decltype(hs_c)::value;
+    constexpr bool PS = decltype(ps_c)::value;
     const int n_ktiles = (a.Skv + 32 * NKW - 1) / (32 * NKW);
-    ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false, NKW, HS>),
-                dim3(n_ktiles * BHk), dim3(64 * NKW * HS), a.stream, (const uint16_t*)a.q,
-                (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
-                (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv, BHk, a.Hq, a.Hkv, a.Sq,
-                Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh, a.scale, sl2, rows_pad,
-                diag, nullptr);
+    ATTN_LAUNCH(1, (bwd_dkdv_kernel<D, AS_CAUSAL, WIN, BIAS, false, NKW, HS, PS>),
+                dim3(n_ktiles * BHk * (PS ? hsplit : 1)), dim3(64 * NKW * HS), a.stream,
+                (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                (const uint16_t*)a.d_o, (const float*)a.ws, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                BHk, a.Hq, a.Hkv, a.Sq, Sqp, a.Skv, a.window, a.bias, a.bias_sb, a.bias_sh,
+                a.scale, sl2, rows_pad, diag, nullptr, PS ? hsplit : 1,
+                PS ? part : nullptr);
+    if constexpr (PS) {
+      if (hipPeekAtLastError() != hipSuccess) return;
+      const int64_t nkv = (int64_t)BHk * a.Skv * D;
+      const int64_t blocks = std::min<int64_t>((2 * nkv / 8 + 255) / 256, 2048);
+      ATTN_LAUNCH(2, bwd_dkdv_reduce_kernel<D>, dim3((unsigned)blocks), dim3(256), a.stream,
+                  (const float*)part, (uint16_t*)a.dk, (uint16_t*)a.dv, nkv, hsplit);
+    }
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
+  using F = std::false_type;
+  using T = std::true_type;
+  constexpr bool CAN_SPLIT = !WIN && !BIAS;
   if constexpr (D <= 128) {
-    int nkw, hs;
-    bwd_dkdv_config(a, &nkw, &hs);
-    if (nkw == 2 && hs == 4)
-      dkdv(I2{}, I4{});
-    else if (nkw == 4 && hs == 2)
-      dkdv(I4{}, I2{});
-    else
-      dkdv(I4{}, I1{});
+    if (CAN_SPLIT && hsplit > 1) {
+      if constexpr (CAN_SPLIT) {
+        if (nkw == 2 && hs == 4)
+          dkdv(I2{}, I4{}, T{});
+        else if (nkw == 4 && hs == 2)
+          dkdv(I4{}, I2{}, T{});
+        else
+          dkdv(I4{}, I1{}, T{});
+      }
+    } else if (nkw == 2 && hs == 4) {
+      dkdv(I2{}, I4{}, F{});
+    } else if (nkw == 4 && hs == 2) {
+      dkdv(I4{}, I2{}, F{});
+    } else {
+      dkdv(I4{}, I1{}, F{});
+    }
   } else {
-    dkdv(I4{}, I1{});
+    if constexpr (CAN_SPLIT) {
+      if (hsplit > 1) {
+        dkdv(I4{}, I1{}, T{});
+        return hipGetLastError();
+      }
+    }
+    dkdv(I4{}, I1{}, F{});
   }
   return hipGetLastError();
 }

@@ -63,8 +63,10 @@ struct BwdArgs {
   const float* bias;  // as in FwdArgs
   int64_t bias_sb, bias_sh;
   float scale;
-  float* ws;  // [B, Hq, Sqp] pairs (D = rowsum(dO * O), -LSE * log2(e)); Sqp = Sq rounded up to 32
+  float* ws;  // [B, Hq, Sqp] pairs (D = rowsum(dO * O), -LSE * log2(e)); Sqp = Sq rounded up to 32,
+              // then (head split) float32 dK/dV partials
   hipStream_t stream;
+  size_t ws_bytes = 0;  // the workspace's size (attn_bwd): bounds the head split
 };
 
 // Compute units of the current device (256 if the query fails).
@@ -96,11 +98,16 @@ hipError_t launch_bwd(const BwdArgs& a);
 // (nkw) and wave groups that split the query iterations (hs): (4, 1), or
 // (4, 2) / (2, 4) on grids of fewer 128-key workgroups than compute units;
 // and a per-thread override for sweeps and tests ((0, 0) = none).
-void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs);
+void bwd_dkdv_config(const BwdArgs& a, int* nkw, int* hs, int* hsplit);
+// Head split of the dK/dV kernel (plain calls): float32 partials of dK and
+// dV per share of the query heads, at this offset (floats) in the backward
+// workspace: [hsplit][2][B, Hkv, Skv, d].  The workspace for a split of p.
+int64_t bwd_split_part_offset(int B, int Hq, int Sq);
+size_t bwd_split_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int d, int p);
 // The same for the dQ kernel: 32-row query blocks per workgroup (nqw) and
 // wave groups that split the key tiles (hs).
 void bwd_dq_config(const BwdArgs& a, int* nqw, int* hs);
-void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs);
+void bwd_set_tile_override(int nkw, int hs, int nqw, int qhs, int hsplit);
 hipError_t launch_bwd_d256(const BwdArgs& a);   // d = 256 (bwd256.hip)
 // Fused variant (no window or bias): ws holds the (D, nl) pairs, then from
 // bwd_fused_acc_offset floats on the fp32 dQ accumulator [B, Hq, Sq, d].

@@ -18,7 +18,7 @@ timed with HIP events recorded around that kernel inside the timed region.
 `cpu_baseline` times the float64 oracle on a bounded sample on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill|small]
+                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill|small|tiles|gqa_bwd]
 """
 from __future__ import annotations
 
@@ -663,8 +663,10 @@ def bench_gqa_bwd(args, hev, stream, reps):
     """Backward with grouped heads (eight query heads per key/value head),
     bf16 causal d128 S4096, on two grids smaller than the chip: B4 Hq32 Hkv4
     (512 128-key workgroups for dK/dV) and B1 Hq32 Hkv4 (128).  Times the
-    library's launch shapes and, for comparison, both kernels forced to the
-    plain (4, 1) shape."""
+    library's launch shapes (wave groups, and the head split when the
+    workspace it asks for holds partial sums: then a third kernel sums them)
+    and, for comparison, both kernels forced to the plain (4, 1) shape
+    without a split."""
     import torch
     import attention_online_softmax_amd as aos
     from attention_online_softmax_amd.inputs import make_qkv
@@ -676,25 +678,29 @@ def bench_gqa_bwd(args, hev, stream, reps):
                                                with_do=True).items()}
         scale = d ** -0.5
         o, lse = aos.attn_fwd(x["q"], x["k"], x["v"], causal=True, scale=scale)
+        base_ws = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+        split_ws = aos.attn_bwd_split_workspace_bytes(B, Hq, Hkv, S, S, d, True)
         g = dict(dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["k"]),
                  dv=torch.empty_like(x["v"]),
-                 ws=torch.empty(aos.attn_bwd_workspace_bytes(B, Hq, S, d), device="cuda",
-                                dtype=torch.uint8))
+                 ws=torch.empty(max(base_ws, split_ws), device="cuda", dtype=torch.uint8))
 
         def bwd(i):
             aos.attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=True, scale=scale,
                          dq=g["dq"], dk=g["dk"], dv=g["dv"], workspace=g["ws"])
 
         out = {"seed": seed}
-        for name, shape in (("picked", (0, 0, 0, 0)), ("plain", (4, 1, 4, 1))):
+        # the picked launch splits the heads when its workspace is the larger
+        nk_picked = 3 if split_ws > base_ws else 2
+        for name, shape, nk in (("picked", (0, 0, 0, 0, 0), nk_picked),
+                                ("plain", (4, 1, 4, 1, 1), 2)):
             aos.attn_bwd_tile_override(*shape)
             try:
                 for i in range(2):
                     bwd(i)
                 torch.cuda.synchronize()
-                _, times, spans = run_calls([("bwd", bwd)], {"bwd": 2}, hev, reps, stream)
+                _, times, spans = run_calls([("bwd", bwd)], {"bwd": nk}, hev, reps, stream)
             finally:
-                aos.attn_bwd_tile_override(0, 0, 0, 0)
+                aos.attn_bwd_tile_override(0, 0, 0, 0, 0)
             q = quantiles([t for t in spans["bwd"] if t is not None])
             kq = quantiles([t[0] for t in times["bwd"]])["median"]
             kk = quantiles([t[1] for t in times["bwd"]])["median"]
@@ -703,6 +709,8 @@ def bench_gqa_bwd(args, hev, stream, reps):
             out[name] = {"us": q["median"] * 1e3, "dq_kernel_us": kq * 1e3,
                          "dkdv_kernel_us": kk * 1e3, "TFLOP/s": tf,
                          "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+            if nk == 3:
+                out[name]["dkdv_reduce_kernel_us"] = quantiles([t[2] for t in times["bwd"]])["median"] * 1e3
         del x, o, lse, g
         res[f"B{B}"] = out
     return res

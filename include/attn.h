@@ -223,6 +223,19 @@ attn_status attn_decode_noalloc(int dtype, const void* q, const void* k_cache,
  * Returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
 
+/* The larger workspace that lets attn_bwd split the query heads of each
+ * key/value head over several dK/dV workgroups per key tile (calls without
+ * window and bias, on grids too small to fill the device: grouped heads,
+ * few key/value heads): the pairs above, rounded up to 256 bytes, then p x 2
+ * x B x Hkv x Skv x d float32 partial sums of dK and dV, for the split p
+ * the library picks for this shape on the current device, or the one that
+ * attn_bwd_tile_override forces on the calling thread (the plain size when
+ * there is none).  attn_bwd takes the largest split its estimate
+ * prefers that fits the workspace it is given.  Needs a current HIP device
+ * (compute-unit count); returns 0 for invalid sizes. */
+size_t attn_bwd_split_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                                      int causal);
+
 /*
  * Backward.  Gradients of O = softmax(scale Q K^T + C) V given dO, with the
  * probabilities recomputed from the saved lse instead of being stored
@@ -235,7 +248,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq, int d);
  *   lse [B, Hq, Sq]   float32 input
  *   dq  [B, Hq, Sq, d], dk, dv [B, Hkv, Skv, d]   outputs, input dtype
  *   workspace >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned; that
- *   size must stay below 4 GiB (else ATTN_ERR_SHAPE).
+ *   size must stay below 4 GiB (else ATTN_ERR_SHAPE).  A workspace of
+ *   attn_bwd_split_workspace_bytes(...) bytes allows the head split (then a
+ *   third kernel adds the partials into dk and dv).
  * causal, window and bias as in attn_fwd (the same mask as the forward
  * call; no gradient is formed for the bias).  Rows with lse = -inf (no
  * allowed key) contribute nothing.
@@ -318,17 +333,20 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split);
 
 /*
  * attn_bwd_tile_override: for the calling host thread, force the launch
- * shapes of the two backward kernels on later attn_bwd calls at d <= 128
- * (for sweeps and tests).  dK/dV: nkw 32-key blocks per workgroup and hs
- * groups of nkw waves, each group taking every hs-th (query head, query
- * tile) iteration; dQ: nqw 32-row query blocks per workgroup and qhs groups
- * of nqw waves, each group taking every qhs-th key tile.  The groups' sums
- * are added in LDS at the end.  Each pair is (4, 1) (the plain kernel),
- * (4, 2) or (2, 4) (eight waves, the shapes the library takes on grids too
- * small to fill the compute units), or (0, 0) for the library's choice;
- * d = 256 always runs (4, 1).  ATTN_ERR_VALUE for any other pair.
+ * shapes of the two backward kernels on later attn_bwd calls (for sweeps
+ * and tests).  dK/dV: nkw 32-key blocks per workgroup and hs groups of nkw
+ * waves, each group taking every hs-th (query head, query tile) iteration;
+ * dQ: nqw 32-row query blocks per workgroup and qhs groups of nqw waves,
+ * each group taking every qhs-th key tile.  The groups' sums are added in
+ * LDS at the end.  Each pair is (4, 1) (the plain kernel), (4, 2) or
+ * (2, 4) (eight waves, the shapes the library takes on grids too small to
+ * fill the compute units), or (0, 0) for the library's choice; d = 256
+ * always runs (4, 1).  hsplit: the head split of the dK/dV kernel, 1 to 8
+ * workgroups per key tile (0 = the library's choice; calls with window or
+ * bias never split; a call whose workspace cannot hold the forced split
+ * returns ATTN_ERR_WORKSPACE).  ATTN_ERR_VALUE for any other value.
  */
-attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs);
+attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs, int hsplit);
 
 /*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles
@@ -339,7 +357,8 @@ attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs);
  * the caller reads the intervals with hipEventElapsedTime.  Kernels per call: attn_fwd 1
  * (the forward kernel), attn_decode and attn_decode_paged 2 (split,
  * combine), attn_bwd 2
- * (dQ together with D = rowsum(dO*O), then dK/dV), attn_bwd_fused 3.  Pass NULL or n = 0 to stop.  The library
+ * (dQ together with D = rowsum(dO*O), then dK/dV; 3 with the head split:
+ * then the partials' sum), attn_bwd_fused 3.  Pass NULL or n = 0 to stop.  The library
  * neither creates nor destroys the events.  Returns ATTN_ERR_VALUE if n < 0.
  */
 attn_status attn_set_timing_events(void* const* events, int n);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert aos.attn_abi_version() == 4
+    assert aos.attn_abi_version() == 5
     for s in range(9):
         assert aos.attn_status_str(s) and aos.attn_status_str(s) != "unknown status"
     assert aos.attn_status_str(99) == "unknown status"
@@ -195,16 +195,38 @@ def test_fwd_tile_entry_points():
 
 def test_bwd_tile_override_values():
     """Backward launch shapes: (0, 0), (4, 1), (4, 2) and (2, 4) only, for
-    dK/dV and for dQ."""
+    dK/dV and for dQ; the head split 0 to 8."""
     L = aos.lib()
     good = ((4, 1), (4, 2), (2, 4), (0, 0))
     for a in good:
         for b in good:
-            assert L.attn_bwd_tile_override(*a, *b) == 0
+            assert L.attn_bwd_tile_override(*a, *b, 0) == 0
+    for p in range(9):
+        assert L.attn_bwd_tile_override(0, 0, 0, 0, p) == 0
+    for p in (-1, 9, 16):
+        assert L.attn_bwd_tile_override(0, 0, 0, 0, p) == VALUE
     for bad in ((2, 2), (4, 4), (8, 1), (0, 1), (4, 0), (-4, 1), (1, 8)):
-        assert L.attn_bwd_tile_override(*bad, 0, 0) == VALUE
-        assert L.attn_bwd_tile_override(0, 0, *bad) == VALUE
-    assert L.attn_bwd_tile_override(0, 0, 0, 0) == 0
+        assert L.attn_bwd_tile_override(*bad, 0, 0, 0) == VALUE
+        assert L.attn_bwd_tile_override(0, 0, *bad, 0) == VALUE
+    assert L.attn_bwd_tile_override(0, 0, 0, 0, 0) == 0
+
+
+def test_bwd_split_workspace_bytes():
+    """The split workspace is at least the plain one, a multiple of 256 bytes,
+    the plain one for shapes that never split (no grouped heads
+    to deal out, or grids that fill the device), and 0 for invalid sizes."""
+    plain = aos.attn_bwd_workspace_bytes(1, 32, 4096, 128)
+    split = aos.attn_bwd_split_workspace_bytes(1, 32, 4, 4096, 4096, 128, True)
+    assert split >= plain and split % 256 == 0
+    # eight query heads per key/value head over 32 key tiles: the split pays
+    nkv = 1 * 4 * 4096 * 128
+    assert split > plain and (split - plain) % (2 * nkv * 4) < 256
+    # one query head per key/value head: nothing to split
+    assert (aos.attn_bwd_split_workspace_bytes(1, 8, 8, 2048, 2048, 128, True) ==
+            aos.attn_bwd_workspace_bytes(1, 8, 2048, 128))
+    assert aos.attn_bwd_split_workspace_bytes(0, 8, 8, 64, 64, 128, True) == 0
+    assert aos.attn_bwd_split_workspace_bytes(1, 8, 3, 64, 64, 128, True) == 0
+    assert aos.attn_bwd_split_workspace_bytes(1, 8, 8, 65, 64, 128, True) == 0
 
 
 def test_decode_paged_validation():

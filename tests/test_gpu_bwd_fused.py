@@ -20,7 +20,7 @@ def bwd_plain(*args, **kw):
     fused kernel is that shape with dQ folded in, so their dK and dV agree
     bit for bit (the grouped shapes a small grid may take add the groups'
     sums in another order)."""
-    aos.attn_bwd_tile_override(4, 1, 0, 0)
+    aos.attn_bwd_tile_override(4, 1, 0, 0, 1)
     try:
         return aos.attn_bwd(*args, **kw)
     finally:

@@ -58,7 +58,7 @@ def test_dkdv_shapes_parity(case):
     try:
         for kv, qs in SHAPES:
             note(f"bwd shapes dK/dV {kv} dQ {qs} {case}")
-            aos.attn_bwd_tile_override(*kv, *qs)
+            aos.attn_bwd_tile_override(*kv, *qs, 1)
             dq, dk, dv = aos.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
                                       causal=causal, scale=scale, window=W, bias=bg)
             torch.cuda.synchronize()
@@ -87,7 +87,7 @@ def test_bwd_shapes_guard_regions():
     try:
         for kv, qs in SHAPES[1:]:
             note(f"bwd guard dK/dV {kv} dQ {qs}")
-            aos.attn_bwd_tile_override(*kv, *qs)
+            aos.attn_bwd_tile_override(*kv, *qs, 1)
             bufs, views = [], []
             for shape in ((B, Hq, Sq, d), (B, Hkv, Skv, d), (B, Hkv, Skv, d)):
                 n = shape[0] * shape[1] * shape[2] * shape[3]

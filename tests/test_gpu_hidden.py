@@ -314,7 +314,7 @@ def test_bwd_hidden(case):
     o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
     bwd = aos.attn_bwd_fused if mode == "fused" else aos.attn_bwd
     if mode == "plain":
-        aos.attn_bwd_tile_override(4, 1, 4, 1)
+        aos.attn_bwd_tile_override(4, 1, 4, 1, 1)
     try:
         dq, dk, dv = bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal,
                          scale=scale)
