@@ -88,6 +88,16 @@ __device__ __forceinline__ void store_transposed_f32(float* rowp, const f32x16* 
 template <int D>
 constexpr int kBwdMinWaves = D >= 256 ? 1 : 2;
 
+// The fused dK/dV kernel at d = 128: its dQ products (and a window's or a
+// bias's state) do not fit 256 registers next to the dK and dV
+// accumulators (it spilled 8 to 175 registers), so it runs at one wave per
+// SIMD with the accumulation registers as well.  On B4 H16 S2048: window
+// 512 with a bias 496 -> 365 us, the bias alone 671 -> 574 us, causal 541
+// -> 520 us.  The two-kernel dK/dV kernel with a window and a bias keeps two
+// waves per SIMD and its 8-register spill: at one wave it was 13 % slower.
+template <int D, bool FUSED>
+constexpr int kBwdDkdvMinWaves = (FUSED && D == 128) ? 1 : kBwdMinWaves<D>;
+
 // Small grids (fewer 128-key workgroups than compute units, e.g. grouped
 // heads with few key/value heads): NKW 32-key blocks per workgroup and HS
 // groups of NKW waves.  Group h takes every HS-th iteration (query head,
@@ -103,7 +113,7 @@ constexpr int kBwdMinWaves = D >= 256 ? 1 : 2;
 // adds the partials and rounds them to dK and dV.
 template <int D, bool CAUSAL, bool WIN, bool BIAS, bool FUSED, int NKW = 4, int HS = 1,
           bool PS = false>
-__global__ __launch_bounds__(64 * NKW * HS, (kBwdMinWaves<D>)) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NKW * HS, (kBwdDkdvMinWaves<D, FUSED>)) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int BHk, int Hq, int Hkv, int Sq, int Sqp, int Skv, int window,
