@@ -18,7 +18,7 @@ timed with HIP events recorded around that kernel inside the timed region.
 `cpu_baseline` times the float64 oracle on a bounded sample on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill|small|tiles|gqa_bwd]
+                       [--no-extras] [--only fwd_bwd|decode|paged_decode|prefill|small|tiles|gqa_bwd|fused_bwd]
 """
 from __future__ import annotations
 
@@ -47,6 +47,7 @@ KERNELS = {
 }
 SOURCES = {"fwd_bf16_kernel": "fwd.hip",
            "bwd_dkdv_kernel": "bwd_kernels.h", "bwd_dq_kernel": "bwd_kernels.h",
+           "bwd_dkdv_fused_kernel": "bwd_kernels.h",
            "decode_split_kernel": "decode.hip", "decode_combine_kernel": "decode.hip"}
 
 
@@ -947,7 +948,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--only", choices=["fwd_bwd", "decode", "paged_decode", "prefill", "small",
-                                       "tiles", "gqa_bwd"], default=None)
+                                       "tiles", "gqa_bwd", "fused_bwd"], default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -986,6 +987,9 @@ def main():
         return
     if args.only == "gqa_bwd":
         print(json.dumps(bench_gqa_bwd(args, hev, stream, args.steps)), flush=True)
+        return
+    if args.only == "fused_bwd":
+        print(json.dumps(strip(bench_fused_bwd(args, hev, stream, args.steps))), flush=True)
         return
 
     w, cpu0, r = bench_fwd_bwd(args, hev, stream)
