@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     attn_fwd_tile_override,
     attn_bwd_tile_override,
     attn_bwd_split_workspace_bytes,
+    attn_bwd_plan,
     attn_fwd_tile_plan,
     attn_set_timing_events,
     attn_status_str,

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 }
 EXPORTS = ("attn_abi_version", "attn_status_str", "attn_supports", "attn_fwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_paged",
-           "attn_bwd_workspace_bytes", "attn_bwd_split_workspace_bytes", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_bwd_split_workspace_bytes", "attn_bwd_plan",
+           "attn_bwd",
            "attn_bwd_fused_workspace_bytes",
            "attn_bwd_fused", "attn_set_timing_events", "attn_decode_noalloc",
            "attn_fwd_tile_plan", "attn_fwd_tile_override", "attn_bwd_tile_override")
@@ -86,6 +87,8 @@ def lib():
     L.attn_bwd_tile_override.argtypes = [i, i, i, i, i]
     L.attn_bwd_split_workspace_bytes.restype = sz
     L.attn_bwd_split_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_bwd_plan.restype = i
+    L.attn_bwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, sz] + [ctypes.POINTER(i)] * 5
     L.attn_set_timing_events.restype = i
     L.attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     _lib = L
@@ -348,6 +351,25 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv
 
 def attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, causal):
     return int(lib().attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, int(bool(causal))))
+
+
+def attn_bwd_plan(B, Hq, Hkv, Sq, Skv, d, causal, window=0, bias=False, workspace_bytes=None):
+    """The launch attn_bwd would make: {"dkdv": (nkw, hs), "dq": (nqw, qhs),
+    "hsplit": p}.  workspace_bytes defaults to the size attn_bwd allocates
+    itself when given none (the split workspace for calls without window or
+    bias).  Raises AttnError with the status attn_bwd would return."""
+    if workspace_bytes is None:
+        workspace_bytes = attn_bwd_workspace_bytes(B, Hq, Sq, d)
+        if window <= 0 and not bias:
+            workspace_bytes = max(workspace_bytes,
+                                  attn_bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, causal))
+    out = [ctypes.c_int() for _ in range(5)]
+    st = lib().attn_bwd_plan(B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), int(window),
+                             int(bool(bias)), int(workspace_bytes), *[ctypes.byref(x) for x in out])
+    if st != 0:
+        raise AttnError(st, "attn_bwd_plan")
+    v = [x.value for x in out]
+    return {"dkdv": (v[0], v[1]), "dq": (v[2], v[3]), "hsplit": v[4]}
 
 
 def attn_bwd_fused_workspace_bytes(B, Hq, Sq, d):

@@ -552,6 +552,38 @@ size_t attn_bwd_split_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, i
   return attn::bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, hsplit);
 }
 
+attn_status attn_bwd_plan(int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
+                          int has_bias, size_t workspace_bytes, int* nkw, int* hs, int* nqw,
+                          int* qhs, int* hsplit) {
+  if (!nkw || !hs || !nqw || !qhs || !hsplit) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Skv) return ATTN_ERR_SHAPE;
+  if (window > 0 && !causal) return ATTN_ERR_VALUE;
+  if (!sizes_ok(Sq, d) || !sizes_ok(Skv, d)) return ATTN_ERR_SHAPE;
+  if (attn_bwd_workspace_bytes(B, Hq, Sq, d) > 0xffffffffu) return ATTN_ERR_SHAPE;
+  if (!bwd_d_ok(ATTN_BF16, d)) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Sq, d)) return ATTN_ERR_WORKSPACE;
+  // Only whether a bias is given matters to the plan, never its values.
+  static const float no_values = 0.f;
+  attn::BwdArgs a{ATTN_BF16, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, B, Hq, Hkv, Sq, Skv, d, causal ? 1 : 0,
+                  window > 0 && window < Skv ? window : 0, has_bias ? &no_values : nullptr, 0, 0,
+                  1.f, nullptr, nullptr, workspace_bytes};
+  attn::bwd_dkdv_config(a, nkw, hs, hsplit);
+  if (d <= 128) {
+    attn::bwd_dq_config(a, nqw, qhs);
+  } else {
+    *nkw = 4;
+    *hs = 1;
+    *nqw = 4;
+    *qhs = 1;
+  }
+  if (workspace_bytes < attn::bwd_split_workspace_bytes(B, Hq, Hkv, Sq, Skv, d, *hsplit))
+    return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
 size_t attn_bwd_fused_workspace_bytes(int B, int Hq, int Sq, int d) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0) return 0;
   return round256((size_t)attn::bwd_fused_acc_offset(B, Hq, Sq) * sizeof(float) +

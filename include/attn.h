@@ -349,6 +349,26 @@ attn_status attn_fwd_tile_override(int nw, int bc, int split);
 attn_status attn_bwd_tile_override(int nkw, int hs, int nqw, int qhs, int hsplit);
 
 /*
+ * attn_bwd_plan: the launch attn_bwd would make for a call of this shape on
+ * the current device from the calling thread (its tile override included),
+ * without launching anything: the dK/dV kernel's (nkw, hs), the dQ kernel's
+ * (nqw, qhs), as in attn_bwd_tile_override, and the head split hsplit (1 =
+ * none, then two kernels; else a third adds the partials).  window as in
+ * attn_bwd; has_bias != 0 for a call that passes a bias (only its presence
+ * matters); workspace_bytes the size of the workspace the call would get:
+ * attn_bwd_workspace_bytes(...) never splits, attn_bwd_split_workspace_bytes
+ * (...) allows the split the library prefers.  Status as attn_bwd would
+ * return it for the sizes (ATTN_ERR_SHAPE, ATTN_ERR_VALUE,
+ * ATTN_ERR_UNSUPPORTED for a head dim without a backward, ATTN_ERR_WORKSPACE
+ * for a workspace below the plain size or one that cannot hold a forced
+ * split), ATTN_ERR_NULL for a NULL output.  Without a HIP device the
+ * estimate assumes 256 compute units.
+ */
+attn_status attn_bwd_plan(int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, int window,
+                          int has_bias, size_t workspace_bytes, int* nkw, int* hs, int* nqw,
+                          int* qhs, int* hsplit);
+
+/*
  * Diagnostics: per-kernel timing.  `events` points to n hipEvent_t handles
  * created by the caller.  While set (per calling host thread), every entry
  * point binds events[2i] and events[2i+1] (those with index < n) to the i-th

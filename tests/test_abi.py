@@ -345,3 +345,115 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         bnd.lib()
+
+
+# The backward's launch choices measured fastest on MI355X (256 compute
+# units, which the plan assumes without a device): (B, Hq, Hkv, S, d, causal)
+# -> dK/dV shape, dQ shape, with the plain workspace (no head split).
+BWD_SHAPE_PICKS = [
+    ((1, 32, 4, 4096, 128, True), (2, 4), (4, 1)),
+    ((1, 16, 2, 2048, 128, True), (2, 4), (2, 4)),
+    ((1, 8, 1, 8192, 128, True), (2, 4), (4, 1)),
+    ((1, 64, 8, 6144, 128, True), (2, 4), (4, 1)),
+    ((2, 16, 4, 4096, 128, True), (2, 4), (4, 1)),
+    ((2, 32, 8, 1024, 64, True), (2, 4), (4, 1)),
+    ((4, 32, 8, 4096, 128, True), (4, 1), (4, 1)),
+    ((2, 8, 8, 1024, 64, True), (2, 4), (2, 4)),
+    ((2, 16, 16, 512, 128, True), (2, 4), (2, 4)),
+    ((1, 12, 12, 2048, 128, True), (2, 4), (2, 4)),
+    ((2, 16, 16, 1536, 128, True), (4, 2), (4, 1)),
+    ((2, 16, 16, 2048, 128, True), (4, 2), (4, 1)),
+    ((1, 16, 16, 2048, 128, False), (4, 2), (4, 1)),
+    ((3, 16, 16, 2048, 128, True), (4, 1), (4, 1)),
+    ((1, 40, 40, 2048, 128, True), (4, 1), (4, 1)),
+    ((4, 16, 16, 2048, 128, True), (4, 1), (4, 1)),
+    ((8, 16, 16, 2048, 64, True), (4, 1), (4, 1)),
+    ((1, 32, 32, 2048, 64, False), (4, 1), (4, 1)),
+]
+
+# The head split with the workspace of attn_bwd_split_workspace_bytes: the
+# split the library takes, each within run-to-run noise of the fastest
+# measured on MI355X.
+BWD_SPLIT_PICKS = [
+    ((1, 16, 2, 2048, 128, True), 8),
+    ((1, 32, 4, 4096, 128, True), 4),
+    ((2, 32, 4, 4096, 128, True), 4),
+    ((4, 32, 4, 4096, 128, True), 4),
+    ((1, 16, 2, 4096, 128, False), 8),
+    ((1, 32, 8, 2048, 64, True), 2),
+    ((2, 16, 2, 4096, 256, True), 4),
+    ((1, 16, 2, 8192, 256, True), 4),
+    ((1, 64, 8, 4096, 128, True), 4),
+    ((4, 16, 16, 2048, 128, True), 1),
+]
+
+
+@pytest.mark.parametrize("shape,kv,q", BWD_SHAPE_PICKS, ids=lambda v: str(v))
+def test_bwd_plan_wave_groups(shape, kv, q):
+    B, Hq, Hkv, S, d, causal = shape
+    plain = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+    plan = aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, causal, workspace_bytes=plain)
+    assert plan == {"dkdv": kv, "dq": q, "hsplit": 1}
+
+
+@pytest.mark.parametrize("shape,p", BWD_SPLIT_PICKS, ids=lambda v: str(v))
+def test_bwd_plan_head_split(shape, p):
+    B, Hq, Hkv, S, d, causal = shape
+    plan = aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, causal)
+    assert plan["hsplit"] == p
+    if d > 128:
+        assert plan["dkdv"] == (4, 1) and plan["dq"] == (4, 1)
+    # the split workspace holds exactly the pairs and p float32 copies of dK, dV
+    plain = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+    split = aos.attn_bwd_split_workspace_bytes(B, Hq, Hkv, S, S, d, causal)
+    want = plain if p == 1 else (plain + 255) // 256 * 256 + p * 2 * B * Hkv * S * d * 4
+    assert split == (want + 255) // 256 * 256 if p > 1 else split == plain
+
+
+def test_bwd_plan_never_splits():
+    """No split with a window, a bias, the plain workspace or one query head
+    per key/value head."""
+    B, Hq, Hkv, S, d = 1, 16, 2, 2048, 128
+    big = 1 << 34
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=big)["hsplit"] > 1
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, window=512, workspace_bytes=big)["hsplit"] == 1
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, bias=True, workspace_bytes=big)["hsplit"] == 1
+    plain = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=plain)["hsplit"] == 1
+    assert aos.attn_bwd_plan(1, 8, 8, S, S, d, True, workspace_bytes=big)["hsplit"] == 1
+    # a window of at least Skv keys is no window
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, window=S,
+                             workspace_bytes=big)["hsplit"] > 1
+
+
+def test_bwd_plan_override_and_errors():
+    B, Hq, Hkv, S, d = 1, 16, 2, 1024, 128
+    big = 1 << 34
+    plain = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+    aos.attn_bwd_tile_override(4, 2, 2, 4, 3)
+    try:
+        assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=big) == {
+            "dkdv": (4, 2), "dq": (2, 4), "hsplit": 3}
+        # a forced split the workspace cannot hold
+        with pytest.raises(aos.AttnError) as e:
+            aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=plain)
+        assert e.value.status == 6
+        # d = 256 keeps the plain shapes, forced or not
+        assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, 256, True, workspace_bytes=big) == {
+            "dkdv": (4, 1), "dq": (4, 1), "hsplit": 3}
+    finally:
+        aos.attn_bwd_tile_override(0, 0, 0, 0, 0)
+    assert aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=big)["hsplit"] == 8
+    for kw, status in ((dict(Hkv=3), 2), (dict(d=96), 3), (dict(causal=False, window=64), 8),
+                       (dict(ws=plain - 16), 6), (dict(Sq=S + 1), 2)):
+        a = dict(B=B, Hq=Hq, Hkv=Hkv, Sq=S, Skv=S, d=d, causal=True, window=0, ws=big)
+        a.update(kw)
+        with pytest.raises(aos.AttnError) as e:
+            aos.attn_bwd_plan(a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["d"], a["causal"],
+                              window=a["window"], workspace_bytes=a["ws"])
+        assert e.value.status == status, kw
+    L = aos.lib()
+    import ctypes
+    x = ctypes.c_int()
+    assert L.attn_bwd_plan(B, Hq, Hkv, S, S, d, 1, 0, 0, big, None, ctypes.byref(x),
+                           ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == 1

@@ -103,3 +103,34 @@ def test_head_split_needs_its_workspace():
                          workspace=ws)
     finally:
         aos.attn_bwd_tile_override(0, 0, 0, 0, 0)
+
+
+def test_launch_follows_the_plan():
+    """attn_bwd_plan says whether a call splits; the call's third kernel (the
+    partials' sum) runs exactly then.  Events bound to kernel slot 2 are
+    recorded before the call: they are recorded again after the dK/dV
+    kernel only if that kernel is launched."""
+    B, Hq, Hkv, S, d = 1, 16, 2, 1024, 128
+    dev, _ = inputs(B, Hq, Hkv, S, S, d, "bf16", 2600, with_do=True)
+    o, lse = aos.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    big = aos.attn_bwd_split_workspace_bytes(B, Hq, Hkv, S, S, d, True)
+    small = aos.attn_bwd_workspace_bytes(B, Hq, S, d)
+    for ws_bytes in (big, small):
+        plan = aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=ws_bytes)
+        assert (plan["hsplit"] > 1) == (ws_bytes == big)
+        note(f"bwd launch vs plan {plan}")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        aos.attn_set_timing_events([e.cuda_event for e in evs])
+        try:
+            aos.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True,
+                         workspace=torch.empty(ws_bytes, dtype=torch.uint8, device="cuda"))
+        finally:
+            aos.attn_set_timing_events(None)
+        torch.cuda.synchronize()
+        # the dK/dV kernel (slot 1) ran after the dQ kernel (slot 0)
+        assert evs[0].elapsed_time(evs[3]) > 0
+        third_ran = evs[3].elapsed_time(evs[4]) >= 0 and evs[3].elapsed_time(evs[5]) > 0
+        assert third_ran == (plan["hsplit"] > 1)
