@@ -692,6 +692,8 @@ def bench_gqa_bwd(args, hev, stream, reps):
         out = {"seed": seed}
         # the picked launch splits the heads when its workspace is the larger
         nk_picked = 3 if split_ws > base_ws else 2
+        plan = aos.attn_bwd_plan(B, Hq, Hkv, S, S, d, True, workspace_bytes=max(base_ws, split_ws))
+        assert (plan["hsplit"] > 1) == (nk_picked == 3)
         for name, shape, nk in (("picked", (0, 0, 0, 0, 0), nk_picked),
                                 ("plain", (4, 1, 4, 1, 1), 2)):
             aos.attn_bwd_tile_override(*shape)
@@ -712,6 +714,9 @@ def bench_gqa_bwd(args, hev, stream, reps):
                          "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
             if nk == 3:
                 out[name]["dkdv_reduce_kernel_us"] = quantiles([t[2] for t in times["bwd"]])["median"] * 1e3
+            if name == "picked":
+                out[name]["plan"] = {"dkdv": list(plan["dkdv"]), "dq": list(plan["dq"]),
+                                     "hsplit": plan["hsplit"]}
         del x, o, lse, g
         res[f"B{B}"] = out
     return res
