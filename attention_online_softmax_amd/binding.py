@@ -325,7 +325,14 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, n_
 
 def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
              workspace=None, stream=None, window=0, bias=None):
-    """Backward (same causal / window as the forward call).  Returns (dq, dk, dv)."""
+    """Backward (same causal / window as the forward call).  Returns (dq, dk, dv).
+
+    Without a `workspace`, one is allocated for the call: for calls without
+    window and bias, the size of attn_bwd_split_workspace_bytes, which lets
+    the library deal a key/value head's query heads over several workgroups
+    (float32 partials of dK and dV, up to 8 x 2 x B x Hkv x Skv x d x 4
+    bytes on grids too small to fill the device); else the pairs alone.  Pass
+    a workspace of attn_bwd_workspace_bytes to keep the call within that."""
     _check([q, k, v, o, do, lse], ["q", "k", "v", "o", "do", "lse"])
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
