@@ -8,7 +8,7 @@ scales -- on every entry point and every kernel family (fp32 and bf16
 forward at d = 64, 128, 256, causal and not; the matrix-core, vector-unit and
 paged decodes; the two-kernel and fused backwards).
 
-Tolerances.  The benchmark spec tolerances (fp32 O 1e-5, bf16 O 2e-2, gradients
+Tolerances.  The parity tolerances (fp32 O 1e-5, bf16 O 2e-2, gradients
 5e-2; LSE 1e-5 / 1e-3 by our reading) are absolute and hold for values of
 unit size.  These inputs make scores, LSE and gradients far larger, so the
 tolerances add what the dtypes themselves force:
